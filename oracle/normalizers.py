@@ -92,7 +92,9 @@ def sparsemax_row(s):
         # the element just outside must not exceed the threshold
         assert zs[k] <= tau + 1e-12 * max(1.0, abs(tau)), "sparsemax support inconsistent"
     p = np.maximum(z - tau, 0.0)
-    return p, tau, k
+    # report the size of the support p actually has (they differ only when an
+    # element lies within fp64 rounding of tau)
+    return p, tau, int(np.count_nonzero(p))
 
 
 def entmax15_row(s):
@@ -135,7 +137,7 @@ def entmax15_row(s):
     if k < n:
         assert zs[k] <= tau + 1e-12 * max(1.0, abs(tau)), "entmax15 support inconsistent"
     p = np.maximum(z - tau, 0.0) ** 2
-    return p, tau, k
+    return p, tau, int(np.count_nonzero(z > tau))
 
 
 _ROW_FUNCS = {
