@@ -1,0 +1,201 @@
+"""ctypes binding of libattn (include/attn.h): argument marshalling only.
+
+PyTorch supplies device memory and the stream; every step of the attention
+forward runs in the HIP kernels of libattn.so.  There is no Python or CPU
+implementation behind these functions: if the library is not built they
+raise.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_LAUNCH = range(5)
+NORMALIZER_IDS = {"softmax": 0, "softmax1": 1, "sparsemax": 2, "entmax15": 3}
+_DTYPE_IDS = {torch.float32: 0, torch.bfloat16: 1}
+_DTYPE_UNKNOWN = 99
+
+
+class AttnError(RuntimeError):
+    """A non-zero attn_status returned by libattn."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{attn_strerror(status)} ({detail})")
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class _Paged(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("normalizer", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("scaling", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path=None):
+    """Load libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"libattn.so not found at {path}: build it first "
+                           "(python -m attention_pluggable_normalizers_amd.build)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.attn_fwd.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged), P(_Params),
+                             P(_Tensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                             ctypes.c_void_p]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged),
+                                             P(_Params), P(ctypes.c_size_t)]
+    lib.attn_fwd_workspace_bytes.restype = ctypes.c_int
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_last_error_detail.argtypes = []
+    lib.attn_last_error_detail.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def attn_strerror(status):
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def attn_last_error_detail():
+    return load_library().attn_last_error_detail().decode()
+
+
+def attn_abi_version():
+    return load_library().attn_abi_version()
+
+
+def _desc(t):
+    if t.dim() != 4:
+        raise ValueError("attn tensors are 4-D")
+    d = _Tensor()
+    d.data = t.data_ptr()
+    d.dtype = _DTYPE_IDS.get(t.dtype, _DTYPE_UNKNOWN)
+    d.reserved = 0
+    for i in range(4):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _params(normalizer, causal, window, softcap, scaling, head_dim):
+    p = _Params()
+    p.normalizer = NORMALIZER_IDS.get(normalizer, -1) if isinstance(normalizer, str) else int(normalizer)
+    p.causal = 1 if causal else 0
+    p.window = int(window)
+    p.softcap = float(softcap)
+    p.scaling = float(1.0 / math.sqrt(head_dim) if scaling is None else scaling)
+    return p
+
+
+def _paged_desc(paged):
+    if paged is None:
+        return None
+    pd = _Paged()
+    pd.block_table = paged["block_table"].data_ptr()
+    pd.seq_lens = paged["seq_lens"].data_ptr()
+    pd.block_size = int(paged["block_size"])
+    pd.max_blocks = int(paged["max_blocks"])
+    return pd
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error_detail())
+
+
+def attn_fwd_workspace_bytes(q, k, v, *, normalizer, causal=False, window=0, softcap=0.0,
+                             scaling=None, paged=None):
+    """Workspace bytes ``attn_fwd`` needs for these arguments."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    pd = _paged_desc(paged)
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1])
+    _check(lib.attn_fwd_workspace_bytes(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)),
+                                        ctypes.byref(_desc(v)),
+                                        ctypes.byref(pd) if pd is not None else None,
+                                        ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, window=0,
+             softcap=0.0, scaling=None, paged=None, workspace=None, stream=None):
+    """Enqueue the forward on ``stream`` (default: torch's current stream).
+
+    q [B,Hq,Lq,D]; k, v [B,Hkv,Lk,D], or paged caches [NB,bs,Hkv,D] with
+    ``paged = {"block_table", "seq_lens", "block_size", "max_blocks"}``.
+    ``out`` (allocated like q when None) and ``row_stats`` (float32
+    [B,Hq,Lq,2] or None) receive the results; returns ``(out, row_stats)``.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+                                  or tuple(row_stats.shape) != (*q.shape[:3], 2)):
+        raise ValueError("row_stats must be a contiguous float32 tensor [B, Hq, Lq, 2]")
+    pd = _paged_desc(paged)
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1])
+    if workspace is None:
+        nbytes = attn_fwd_workspace_bytes(q, k, v, normalizer=normalizer, causal=causal,
+                                          window=window, softcap=softcap, scaling=scaling,
+                                          paged=paged)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.attn_fwd(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)), ctypes.byref(_desc(v)),
+                      ctypes.byref(pd) if pd is not None else None, ctypes.byref(p),
+                      ctypes.byref(_desc(out)),
+                      row_stats.data_ptr() if row_stats is not None else None,
+                      ws_ptr, ws_len, stream)
+    _check(st)
+    return out, row_stats
+
+
+def custom_attention(module, query, key, value, attention_mask, *, normalizer, dropout=0.0,
+                     scaling=None, is_causal=True, sliding_window=0, softcap=0.0,
+                     output_attentions=False, **kwargs):
+    """The custom-attention signature of the transformers attention interface.
+
+    ("attention interface", "custom attention registration": the function
+    receives the module, query, key, value and attention_mask and returns
+    ``(attn_output, attn_weights)``; "Attention" (factory.ai), "What every
+    backend must support".)  query [B,Hq,L,D], key/value [B,Hkv,Lk,D] (GQA
+    handled natively).  Only structured masks are supported, so a dense
+    ``attention_mask`` is rejected, as are dropout and returned weights.
+    Returns ``(out [B, L, Hq, D], None)``.
+    """
+    if attention_mask is not None:
+        raise AttnError(ATTN_E_UNSUPPORTED, "dense attention_mask; use is_causal/sliding_window")
+    if dropout:
+        raise AttnError(ATTN_E_UNSUPPORTED, "dropout is not part of this forward")
+    if output_attentions:
+        raise AttnError(ATTN_E_UNSUPPORTED, "attention weights are never materialized")
+    out, _ = attn_fwd(query, key, value, normalizer=normalizer, causal=is_causal,
+                      window=sliding_window or 0, softcap=softcap or 0.0, scaling=scaling)
+    return out.transpose(1, 2).contiguous(), None

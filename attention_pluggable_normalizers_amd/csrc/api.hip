@@ -1,0 +1,199 @@
+// libattn C ABI: argument validation, kernel selection and launch.
+//
+// The selection is a static table on (dtype, head dim, paged, Lq); every
+// accepted request has exactly one kernel family and nothing falls back at
+// run time ("HF Attention Normalizers", "Strict vs Fallback Mode": strict).
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace attn {
+namespace {
+
+thread_local char g_detail[256] = "";
+
+int fail(int status, const char* fmt, const char* what = nullptr) {
+  snprintf(g_detail, sizeof(g_detail), fmt, what ? what : "");
+  return status;
+}
+
+int check_tensor(const attn_tensor* t, const char* name) {
+  if (!t) return fail(ATTN_E_INVALID, "%s descriptor is NULL", name);
+  if (t->reserved != 0) return fail(ATTN_E_INVALID, "%s.reserved must be 0", name);
+  const bool empty = t->shape[0] == 0 || t->shape[1] == 0 || t->shape[2] == 0 || t->shape[3] == 0;
+  if (!t->data && !empty) return fail(ATTN_E_INVALID, "%s data pointer is NULL", name);
+  if (t->dtype != ATTN_F32 && t->dtype != ATTN_BF16)
+    return fail(ATTN_E_UNSUPPORTED, "%s dtype is neither f32 nor bf16", name);
+  for (int d = 0; d < 4; ++d) {
+    if (t->shape[d] < 0) return fail(ATTN_E_INVALID, "%s has a negative extent", name);
+    if (t->stride[d] < 0) return fail(ATTN_E_INVALID, "%s has a negative stride", name);
+  }
+  if (t->stride[3] != 1) return fail(ATTN_E_INVALID, "%s last dimension is not contiguous", name);
+  return ATTN_OK;
+}
+
+// Validates everything and fills the kernel arguments.
+int validate(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+             const attn_paged_kv* paged, const attn_params* p, const attn_tensor* out,
+             float* row_stats, FwdArgs* a, bool need_data) {
+  g_detail[0] = 0;
+  int st;
+  if (!p) return fail(ATTN_E_INVALID, "params pointer is NULL");
+  if (need_data) {
+    if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+        (st = check_tensor(out, "out")))
+      return st;
+  } else {
+    attn_tensor qq, kk, vv;
+    if (!q || !k || !v) return fail(ATTN_E_INVALID, "q, k or v descriptor is NULL");
+    qq = *q; kk = *k; vv = *v;
+    qq.data = kk.data = vv.data = (void*)1;  // sizes only
+    if ((st = check_tensor(&qq, "q")) || (st = check_tensor(&kk, "k")) || (st = check_tensor(&vv, "v")))
+      return st;
+  }
+  if (k->dtype != q->dtype || v->dtype != q->dtype || (out && out->dtype != q->dtype))
+    return fail(ATTN_E_INVALID, "q, k, v and out must share one dtype");
+  if (p->normalizer < ATTN_SOFTMAX || p->normalizer > ATTN_ENTMAX15)
+    return fail(ATTN_E_INVALID, "unknown normalizer");
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
+  if (p->window < 0) return fail(ATTN_E_INVALID, "window must be >= 0");
+  if (p->window > 0 && !p->causal)
+    return fail(ATTN_E_INVALID, "a sliding window requires causal masking");
+  if (!(p->softcap >= 0.f) || !isfinite(p->softcap))
+    return fail(ATTN_E_INVALID, "softcap must be finite and >= 0");
+  if (!isfinite(p->scaling)) return fail(ATTN_E_INVALID, "scaling must be finite");
+
+  const int64_t B = q->shape[0], Hq = q->shape[1], Lq = q->shape[2], D = q->shape[3];
+  int64_t Hkv, Lk;
+  memset(a, 0, sizeof(*a));
+  if (!paged) {
+    if (k->shape[0] != B || v->shape[0] != B) return fail(ATTN_E_INVALID, "k/v batch differs from q");
+    Hkv = k->shape[1];
+    Lk = k->shape[2];
+    if (v->shape[1] != Hkv || v->shape[2] != Lk) return fail(ATTN_E_INVALID, "k and v shapes differ");
+    if (k->shape[3] != D || v->shape[3] != D) return fail(ATTN_E_INVALID, "head dims of q, k, v differ");
+    a->k_sb = k->stride[0]; a->k_sh = k->stride[1]; a->k_sl = k->stride[2];
+    a->v_sb = v->stride[0]; a->v_sh = v->stride[1]; a->v_sl = v->stride[2];
+  } else {
+    if (!paged->block_table || !paged->seq_lens)
+      return fail(ATTN_E_INVALID, "paged block_table or seq_lens is NULL");
+    if (paged->block_size <= 0 || paged->max_blocks <= 0)
+      return fail(ATTN_E_INVALID, "paged block_size and max_blocks must be > 0");
+    if (k->shape[1] != paged->block_size || v->shape[1] != paged->block_size)
+      return fail(ATTN_E_INVALID, "cache slot dimension differs from block_size");
+    if ((int64_t)paged->max_blocks * paged->block_size > (int64_t)INT32_MAX / 2)
+      return fail(ATTN_E_UNSUPPORTED, "max_blocks * block_size too large");
+    Hkv = k->shape[2];
+    Lk = (int64_t)paged->max_blocks * paged->block_size;
+    if (v->shape[0] != k->shape[0] || v->shape[2] != Hkv)
+      return fail(ATTN_E_INVALID, "k and v cache shapes differ");
+    if (k->shape[3] != D || v->shape[3] != D) return fail(ATTN_E_INVALID, "head dims of q, k, v differ");
+    a->k_sb = k->stride[0]; a->k_sl = k->stride[1]; a->k_sh = k->stride[2];
+    a->v_sb = v->stride[0]; a->v_sl = v->stride[1]; a->v_sh = v->stride[2];
+    a->paged = 1;
+    a->block_table = paged->block_table;
+    a->seq_lens = paged->seq_lens;
+    a->block_size = paged->block_size;
+    a->max_blocks = paged->max_blocks;
+  }
+  if (Hkv <= 0 && Hq > 0) return fail(ATTN_E_INVALID, "k/v have no heads");
+  if (Hkv > 0 && Hq % Hkv != 0) return fail(ATTN_E_INVALID, "Hq must be a multiple of Hkv");
+  if (D < 1 || D > 256) return fail(ATTN_E_UNSUPPORTED, "head dim must be in 1..256");
+  if (B > INT32_MAX || Hq > INT32_MAX || Lq > INT32_MAX / 2 || Lk > INT32_MAX / 2)
+    return fail(ATTN_E_UNSUPPORTED, "an extent exceeds the 32-bit index range");
+  if (B * Hq * Lq > (int64_t)INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "too many query rows");
+  if (out) {
+    for (int d = 0; d < 4; ++d)
+      if (out->shape[d] != q->shape[d]) return fail(ATTN_E_INVALID, "out shape differs from q");
+    a->out = out->data;
+    a->o_sb = out->stride[0]; a->o_sh = out->stride[1]; a->o_sl = out->stride[2];
+  }
+  a->q = q->data; a->k = k->data; a->v = v->data;
+  a->q_sb = q->stride[0]; a->q_sh = q->stride[1]; a->q_sl = q->stride[2];
+  a->stats = row_stats;
+  a->dtype = q->dtype;
+  a->B = (int)B; a->Hq = (int)Hq; a->Hkv = (int)Hkv; a->G = Hkv > 0 ? (int)(Hq / Hkv) : 1;
+  a->Lq = (int)Lq; a->Lk = (int)Lk; a->D = (int)D;
+  a->norm = p->normalizer; a->causal = p->causal; a->window = p->window;
+  a->softcap = p->softcap; a->scaling = p->scaling;
+  return ATTN_OK;
+}
+
+enum class Path { kNone, kGeneric, kPrefill, kDecode };
+
+Path select(const FwdArgs& a) {
+  if ((int64_t)a.B * a.Hq * a.Lq == 0) return Path::kNone;
+  if (!a.paged && prefill_mfma_supported(a)) return Path::kPrefill;
+  if (a.paged && decode_supported(a)) return Path::kDecode;
+  return Path::kGeneric;
+}
+
+size_t workspace_for(const FwdArgs& a) {
+  return select(a) == Path::kDecode ? decode_workspace_bytes(a) : 0;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" int attn_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                        const attn_paged_kv* paged, const attn_params* p,
+                        const attn_tensor* out, float* row_stats, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  FwdArgs a;
+  int st = validate(q, k, v, paged, p, out, row_stats, &a, true);
+  if (st) return st;
+  const Path path = select(a);
+  const size_t need = workspace_for(a);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(ATTN_E_WORKSPACE, "workspace smaller than attn_fwd_workspace_bytes()");
+  if (path == Path::kNone) return ATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a launch error left pending on this thread
+  hipError_t e;
+  switch (path) {
+    case Path::kPrefill: e = launch_prefill_mfma(a, s); break;
+    case Path::kDecode: e = launch_decode(a, workspace, s); break;
+    default: e = launch_generic(a, s); break;
+  }
+  if (e != hipSuccess) return fail(ATTN_E_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
+                                        const attn_tensor* v, const attn_paged_kv* paged,
+                                        const attn_params* p, size_t* bytes) {
+  if (!bytes) return fail(ATTN_E_INVALID, "bytes pointer is NULL");
+  attn_paged_kv pk;
+  const attn_paged_kv* pp = paged;
+  if (paged) {  // sizes only: the device pointers are not needed here
+    pk = *paged;
+    if (!pk.block_table) pk.block_table = (const int32_t*)1;
+    if (!pk.seq_lens) pk.seq_lens = (const int32_t*)1;
+    pp = &pk;
+  }
+  FwdArgs a;
+  int st = validate(q, k, v, pp, p, nullptr, nullptr, &a, false);
+  if (st) return st;
+  *bytes = workspace_for(a);
+  return ATTN_OK;
+}
+
+extern "C" const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_E_INVALID: return "ATTN_E_INVALID: invalid argument";
+    case ATTN_E_UNSUPPORTED: return "ATTN_E_UNSUPPORTED: unsupported request";
+    case ATTN_E_WORKSPACE: return "ATTN_E_WORKSPACE: workspace missing or too small";
+    case ATTN_E_LAUNCH: return "ATTN_E_LAUNCH: kernel launch failed";
+    default: return "unknown attn status";
+  }
+}
+
+extern "C" const char* attn_last_error_detail(void) { return g_detail; }
+
+extern "C" int attn_abi_version(void) { return ATTN_ABI_VERSION; }

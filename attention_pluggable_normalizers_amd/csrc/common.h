@@ -1,0 +1,95 @@
+// Internal definitions shared by the libattn kernels and the host dispatcher.
+// Not part of the public ABI (see include/attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace attn {
+
+// Everything a kernel needs, validated and flattened by the dispatcher.
+// Strides are in elements.  For contiguous K/V: (sb, sh, sl) = strides of the
+// batch, head and token dimensions.  For a paged cache [NB, bs, Hkv, D]:
+// sb = page stride, sl = slot stride, sh = head stride.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* stats;
+  int64_t q_sb, q_sh, q_sl;
+  int64_t k_sb, k_sh, k_sl;
+  int64_t v_sb, v_sh, v_sl;
+  int64_t o_sb, o_sh, o_sl;
+  int dtype;  // attn_dtype of q, k, v and out
+  int B, Hq, Hkv, G, Lq, Lk, D;
+  int paged;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int block_size, max_blocks;
+  int norm, causal, window;
+  float softcap, scaling;
+};
+
+typedef __bf16 bf16_t;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }  // RNE
+
+// Wave64 reductions through cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Visible key interval [lo, hi) of query row i when `live` keys exist:
+// bottom-right aligned causal bound and sliding window.
+__device__ __forceinline__ void key_range(int i, int lq, int live, int causal, int window,
+                                          int& lo, int& hi) {
+  const int qp = i + live - lq;
+  int h = causal ? min(live, qp + 1) : live;
+  h = max(h, 0);
+  int l = window ? max(0, qp - window + 1) : 0;
+  lo = min(l, h);
+  hi = h;
+}
+
+// Launchers, one per kernel family (defined in their own translation units).
+hipError_t launch_generic(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const FwdArgs& a, void* workspace, hipStream_t stream);
+size_t decode_workspace_bytes(const FwdArgs& a);
+bool prefill_mfma_supported(const FwdArgs& a);
+bool decode_supported(const FwdArgs& a);
+
+}  // namespace attn

@@ -1,0 +1,170 @@
+/*
+ * attn.h -- C ABI of libattn: the fused attention forward with a pluggable
+ * normalizer, for AMD Instinct MI355X (gfx950).
+ *
+ *     out = N( mask( softcap( scaling * Q K^T ) ) ) V        (grouped-query)
+ *
+ * N is one of softmax, softmax1, sparsemax, 1.5-entmax ("HF Attention
+ * Normalizers", section "Supported Normalizers").  The arguments follow the
+ * backend contract of the transformers "Attention" wiki page (factory.ai,
+ * "What every backend must support": query/key/value after rotary, the mask,
+ * scaling and is_causal; the output) and the paged signature of "HF Attention
+ * Normalizers", "Differentiable Paged Attention" (query, key_cache,
+ * value_cache, block_table, sequence_lengths, block_size, normalizer).
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer.  The library never allocates,
+ *     frees or synchronizes inside attn_fwd; it validates, enqueues kernels on
+ *     the caller's stream and returns.  It keeps no mutable global state apart
+ *     from a thread-local error message, so calls on different streams and
+ *     threads are independent.
+ *   - Pointers: every data pointer is a DEVICE pointer unless stated
+ *     otherwise; the descriptor structs themselves are HOST memory and are only
+ *     read during the call.
+ *   - Errors: strict.  Every entry point returns an attn_status; nothing falls
+ *     back to another path ("HF Attention Normalizers", "Strict vs Fallback
+ *     Mode": unsupported requests raise a clear error).  On an error no kernel
+ *     has been enqueued, except ATTN_E_LAUNCH, which reports the HIP error of
+ *     a launch.  attn_last_error_detail() names the failing check.
+ *   - Dropout and returned attention weights are not part of this forward.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,      /* null pointer, shape/stride/param inconsistency          */
+  ATTN_E_UNSUPPORTED = 2,  /* valid request outside what this build implements        */
+  ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than attn_fwd_workspace_bytes */
+  ATTN_E_LAUNCH = 4        /* a HIP kernel launch failed                               */
+} attn_status;
+
+/* The normalizer N ("Supported Normalizers"):
+ *   SOFTMAX   exp(s_i) / sum_j exp(s_j)
+ *   SOFTMAX1  exp(s_i) / (1 + sum_j exp(s_j))         (Softmax-N with n = 1)
+ *   SPARSEMAX max(s_i - tau, 0),        tau such that the weights sum to 1
+ *   ENTMAX15  max(s_i / 2 - tau, 0)^2,  tau such that the weights sum to 1   */
+typedef enum attn_normalizer {
+  ATTN_SOFTMAX = 0,
+  ATTN_SOFTMAX1 = 1,
+  ATTN_SPARSEMAX = 2,
+  ATTN_ENTMAX15 = 3
+} attn_normalizer;
+
+typedef enum attn_dtype {
+  ATTN_F32 = 0,   /* IEEE binary32                              */
+  ATTN_BF16 = 1   /* bfloat16 (upper half of a binary32)        */
+} attn_dtype;
+
+/* A strided 4-D device tensor.  Strides are in ELEMENTS; the last dimension
+ * must be contiguous (stride[3] == 1) and the other strides >= 0.
+ *   q, out : [B, Hq, Lq, D]
+ *   k, v   : contiguous KV  -> [B, Hkv, Lk, D]
+ *            paged KV       -> caches [num_blocks, block_size, Hkv, D]      */
+typedef struct attn_tensor {
+  void* data;
+  int32_t dtype;         /* attn_dtype; q, k, v and out must agree */
+  int32_t reserved;      /* must be 0 */
+  int64_t shape[4];
+  int64_t stride[4];
+} attn_tensor;
+
+/* Paged KV cache ("Differentiable Paged Attention": the kernel reads the
+ * physical pages through the block table; no gathered K/V is built).
+ * Logical token t of sequence b lives in physical page
+ * block_table[b * max_blocks + t / block_size], slot t % block_size.
+ * Entries past ceil(seq_lens[b] / block_size) are never read (use -1);
+ * slots past seq_lens[b] in the last page are never read.  The host cannot
+ * see seq_lens, so max_blocks * block_size bounds every sequence: a larger
+ * seq_lens[b] is a caller error the kernels clamp to that bound.          */
+typedef struct attn_paged_kv {
+  const int32_t* block_table;  /* device, int32 [B, max_blocks], row-major */
+  const int32_t* seq_lens;     /* device, int32 [B], 0 <= seq_lens[b]      */
+  int32_t block_size;          /* tokens per page, > 0; equals k->shape[1]  */
+  int32_t max_blocks;          /* > 0; row length of block_table           */
+} attn_paged_kv;
+
+/* Forward parameters.
+ *   causal  : keep key j for query i iff j <= i + (L - Lq), L the live key
+ *             count (bottom-right alignment: "Packed Variable-Length
+ *             Attention"; mask_mod "q_idx >= k_idx" of the "attention
+ *             interface" page, "flexattention patterns").
+ *   window  : 0 = none; else also keep only (i + L - Lq) - j < window (the
+ *             sliding-window pattern of the same page).  Requires causal.
+ *   softcap : 0 = none; else score <- softcap * tanh(score / softcap),
+ *             applied after scaling and before the mask ("Attention
+ *             variants", parameter table: logit_softcap).  Must be >= 0.
+ *   scaling : multiplies Q K^T; must be finite.                           */
+typedef struct attn_params {
+  int32_t normalizer;  /* attn_normalizer */
+  int32_t causal;      /* 0 or 1 */
+  int32_t window;      /* >= 0 */
+  float softcap;
+  float scaling;
+} attn_params;
+
+/* attn_fwd -- enqueue the forward on `stream` (a hipStream_t; NULL = the
+ * default stream).
+ *
+ *   q, k, v   : input descriptors (see attn_tensor).  Hq % Hkv == 0; query
+ *               head h reads key/value head h / (Hq / Hkv).
+ *   paged     : NULL for contiguous K/V, else the paged cache descriptor
+ *               (then k, v are the caches; queries align bottom-right
+ *               against each sequence's own length).
+ *   p         : parameters (host struct).
+ *   out       : [B, Hq, Lq, D], same dtype as q, written in full (rows with
+ *               no visible key get zeros).
+ *   row_stats : NULL, or device float32 [B, Hq, Lq, 2], contiguous:
+ *               softmax / softmax1 -> (m, l): the weights are exp(s - m) / l
+ *               (softmax1: m = max(0, max s), l includes exp(-m));
+ *               sparsemax / entmax15 -> (tau, k): threshold (in the s/2
+ *               domain for entmax15) and support size, as a float.
+ *               Rows with no visible key: (-inf, 0), (0, 1), (+inf, 0).
+ *   workspace : device scratch of at least attn_fwd_workspace_bytes(...)
+ *               bytes (may be NULL when that size is 0); its contents on entry
+ *               are ignored and on return are unspecified.  It must not be
+ *               used by another call that runs concurrently.
+ *
+ * Supported: dtype F32 or BF16, D in 1..256, contiguous or paged, any Lq.
+ * BF16 prefill with D in {64, 128, 256} runs on the matrix-core (MFMA)
+ * kernels and BF16 paged decode (Lq == 1) on the split-KV kernels; every
+ * other supported case runs on a plain per-row kernel.
+ * Returns ATTN_OK, or an error code (see attn_status); inputs are not read
+ * and outputs not written on an error other than ATTN_E_LAUNCH.           */
+int attn_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+             const attn_paged_kv* paged, const attn_params* p,
+             const attn_tensor* out, float* row_stats,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_fwd_workspace_bytes -- workspace size attn_fwd needs for these
+ * arguments (host computation only; no device access).  Validates the same
+ * way attn_fwd does and writes the size to *bytes (host pointer).          */
+int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
+                             const attn_tensor* v, const attn_paged_kv* paged,
+                             const attn_params* p, size_t* bytes);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none).
+ * The pointer stays valid until the next call on that thread. */
+const char* attn_last_error_detail(void);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

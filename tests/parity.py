@@ -1,0 +1,145 @@
+"""Helpers for the GPU parity tests: run libattn, run the oracle, compare.
+
+The comparison rule:
+  * out: max-abs error <= 1e-5 for f32 inputs, <= 2e-2 for bf16 inputs;
+  * row statistics: softmax family (m, l) to fp32 rounding; sparse tau to
+    fp32 rounding and the support size k exactly, except for keys whose z
+    lies within 1e-6 of the oracle's tau (the exclusion band), which may
+    land on either side;
+  * weight pattern (one-hot V probe): a key has nonzero weight on the GPU
+    exactly when it has one in the oracle, outside the same band.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+import attention_pluggable_normalizers_amd as apn
+from oracle import attention_forward, paged_attention_forward
+
+TOL_OUT = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+BAND = 1e-6
+
+
+def to_dev(*xs):
+    return [x.to("cuda") for x in xs]
+
+
+def gpu_fwd(q, k, v, norm, causal, window, softcap, scaling, paged=None):
+    """Run libattn on device copies of q, k, v; returns fp64 numpy out and stats."""
+    qd, kd, vd = to_dev(q, k, v)
+    stats = torch.full((*q.shape[:3], 2), float("nan"), dtype=torch.float32, device="cuda")
+    pdev = None
+    if paged is not None:
+        pdev = dict(paged)
+        pdev["block_table"] = paged["block_table"].to("cuda")
+        pdev["seq_lens"] = paged["seq_lens"].to("cuda")
+    out, _ = apn.attn_fwd(qd, kd, vd, None, stats, normalizer=norm, causal=causal,
+                          window=window, softcap=softcap, scaling=scaling, paged=pdev)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), stats.double().cpu().numpy()
+
+
+def band_count(z, tau):
+    if not np.isfinite(tau) or z is None or len(z) == 0:
+        return 0
+    return int(np.sum(np.abs(np.asarray(z) - tau) <= BAND))
+
+
+def compare_stats(st_g, st_o, norm, n_allowed, band=0, where=""):
+    """One row's statistics (n_allowed = number of keys the row may see)."""
+    g0, g1 = float(st_g[0]), float(st_g[1])
+    o0, o1 = float(st_o[0]), float(st_o[1])
+    if n_allowed == 0:
+        assert (g0, g1) == (o0, o1), f"{where}: empty-row stats {(g0, g1)} vs {(o0, o1)}"
+        return
+    if norm in ("softmax", "softmax1"):
+        assert abs(g0 - o0) <= 1e-4 + 1e-5 * abs(o0), f"{where}: m {g0} vs {o0}"
+        assert abs(g1 - o1) <= 1e-4 * abs(o1), f"{where}: l {g1} vs {o1}"
+    else:
+        assert abs(g0 - o0) <= 2e-5 + 1e-6 * abs(o0), f"{where}: tau {g0} vs {o0}"
+        assert abs(g1 - o1) <= band, f"{where}: support {g1} vs {o1} (band {band})"
+
+
+def _band(norm, z, tau):
+    return band_count(z, tau) if norm in ("sparsemax", "entmax15") else 0
+
+
+def check_full(q, k, v, norm, causal=False, window=0, softcap=0.0, scaling=None, where=""):
+    """Whole-tensor parity against the oracle (small and medium shapes)."""
+    if scaling is None:
+        scaling = 1.0 / math.sqrt(q.shape[-1])
+    out_g, st_g = gpu_fwd(q, k, v, norm, causal, window, softcap, scaling)
+    B, Hq, Lq, _ = q.shape
+    rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(Lq)]
+    out_o, st_o, det = attention_forward(q, k, v, norm, causal, window, softcap, scaling,
+                                         rows=rows, return_probs=True)
+    err = np.abs(out_g.reshape(-1, q.shape[-1]) - out_o).max() if out_o.size else 0.0
+    assert err <= TOL_OUT[q.dtype], f"{where} {norm}: out max-abs {err:.3e}"
+    stg = st_g.reshape(-1, 2)
+    for r, (b, h, i) in enumerate(rows):
+        idx, p, z = det[r]
+        compare_stats(stg[r], st_o[r], norm, len(idx), _band(norm, z, st_o[r][0]),
+                      where=f"{where} {norm} row {(b, h, i)}")
+    return err
+
+
+def check_rows(out_g, st_g, rows, q, k, v, norm, causal, window, softcap, scaling, paged=None,
+               where=""):
+    """Parity on sampled rows of a large problem (out and stats)."""
+    if paged is None:
+        out_o, st_o, det = attention_forward(q, k, v, norm, causal, window, softcap, scaling,
+                                             rows=rows, return_probs=True)
+    else:
+        out_o, st_o, det = paged_attention_forward(q, k, v, paged["block_table"].cpu().numpy(),
+                                                   paged["seq_lens"].cpu().numpy(), norm,
+                                                   causal, window, softcap, scaling, rows=rows,
+                                                   return_probs=True)
+    worst = 0.0
+    for r, (b, h, i) in enumerate(rows):
+        e = float(np.abs(out_g[b, h, i] - out_o[r]).max())
+        worst = max(worst, e)
+        assert e <= TOL_OUT[q.dtype], f"{where} {norm} row {(b, h, i)}: out max-abs {e:.3e}"
+        idx, p, z = det[r]
+        compare_stats(st_g[b, h, i], st_o[r], norm, len(idx), _band(norm, z, st_o[r][0]),
+                      where=f"{where} {norm} row {(b, h, i)}")
+    return worst
+
+
+def onehot_probe(q, k, norm, causal, window, softcap, scaling, j0, where=""):
+    """Weight pattern of keys j0 .. j0+D-1 for every row, GPU vs oracle.
+
+    V holds unit vectors, v[j0 + c] = e_c, so out[..., c] is the weight of
+    key j0 + c itself (exact zeros stay exact zeros through the products).
+    """
+    B, Hkv, Lk, D = k.shape
+    v = torch.zeros_like(k)
+    for c in range(D):
+        if j0 + c < Lk:
+            v[:, :, j0 + c, c] = 1.0
+    out_g, _ = gpu_fwd(q, k, v, norm, causal, window, softcap, scaling)
+    _, st_o, P = attention_forward(q, k, v, norm, causal, window, softcap, scaling,
+                                   return_probs=True)
+    ncols = min(D, Lk - j0)
+    got = out_g[..., :ncols] > 0
+    want = P[..., j0:j0 + ncols] > 0
+    mism = got != want
+    if norm in ("sparsemax", "entmax15") and mism.any():
+        # keys inside the exclusion band may go either way
+        s = _scores_for_band(q, k, scaling, softcap)[..., j0:j0 + ncols]
+        z = s / 2.0 if norm == "entmax15" else s
+        tau = st_o[..., 0:1]
+        mism &= ~(np.abs(z - tau) <= BAND)
+    assert not mism.any(), f"{where} {norm}: {int(mism.sum())} pattern mismatches at key block {j0}"
+
+
+def _scores_for_band(q, k, scaling, softcap):
+    """fp64 scores, only to locate keys inside the exclusion band."""
+    qf = q.double().numpy()
+    kf = k.double().numpy()
+    G = qf.shape[1] // kf.shape[1]
+    s = scaling * np.einsum("bhid,bhjd->bhij", qf, np.repeat(kf, G, axis=1))
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
+    return s

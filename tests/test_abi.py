@@ -1,0 +1,168 @@
+"""The C ABI library: it loads, exports what include/attn.h declares, and
+rejects invalid arguments before touching the GPU (host-side checks only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import attention_pluggable_normalizers_amd as apn
+from attention_pluggable_normalizers_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libattn.so is not built (python -m attention_pluggable_normalizers_amd.build)")
+    return B.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names == sorted(["attn_fwd", "attn_fwd_workspace_bytes", "attn_strerror",
+                            "attn_last_error_detail", "attn_abi_version"])
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    assert apn.attn_abi_version() == 1
+    for code in range(5):
+        assert apn.attn_strerror(code).startswith("ATTN_")
+    assert "unknown" in apn.attn_strerror(77)
+
+
+# fake device pointers: validation never dereferences them
+def _t(shape, dtype=torch.bfloat16, strides=None):
+    d = B._Tensor()
+    d.data = 0x1000
+    d.dtype = B._DTYPE_IDS.get(dtype, 99)
+    d.reserved = 0
+    if strides is None:
+        strides = [0] * 4
+        acc = 1
+        for i in (3, 2, 1, 0):
+            strides[i] = acc
+            acc *= shape[i]
+    for i in range(4):
+        d.shape[i] = shape[i]
+        d.stride[i] = strides[i]
+    return d
+
+
+def _p(norm=0, causal=1, window=0, softcap=0.0, scaling=0.125):
+    p = B._Params()
+    p.normalizer, p.causal, p.window, p.softcap, p.scaling = norm, causal, window, softcap, scaling
+    return p
+
+
+def _call(lib, q, k, v, p, out=None, paged=None, ws=0, wsp=None):
+    out = out or q
+    r = lib.attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                     ctypes.byref(paged) if paged else None, ctypes.byref(p), ctypes.byref(out),
+                     None, wsp, ws, None)
+    return r, apn.attn_last_error_detail()
+
+
+Q = (2, 8, 64, 64)
+KV = (2, 2, 64, 64)
+
+
+@pytest.mark.parametrize("mutate,code,needle", [
+    (lambda a: a["p"].__setattr__("normalizer", 7), 1, "normalizer"),
+    (lambda a: a["p"].__setattr__("causal", 2), 1, "causal"),
+    (lambda a: a["p"].__setattr__("window", -1), 1, "window"),
+    (lambda a: (a["p"].__setattr__("window", 4), a["p"].__setattr__("causal", 0)), 1, "causal"),
+    (lambda a: a["p"].__setattr__("softcap", -1.0), 1, "softcap"),
+    (lambda a: a["p"].__setattr__("softcap", float("inf")), 1, "softcap"),
+    (lambda a: a["p"].__setattr__("scaling", float("nan")), 1, "scaling"),
+    (lambda a: a.__setitem__("k", _t((2, 3, 64, 64))), 1, "k and v"),
+    (lambda a: (a.__setitem__("k", _t((2, 3, 64, 64))), a.__setitem__("v", _t((2, 3, 64, 64)))),
+     1, "multiple"),
+    (lambda a: a.__setitem__("v", _t((2, 2, 64, 32))), 1, "head dim"),
+    (lambda a: a.__setitem__("k", _t((1, 2, 64, 64))), 1, "batch"),
+    (lambda a: a.__setitem__("k", _t(KV, torch.float32)), 1, "dtype"),
+    (lambda a: a.__setitem__("q", _t(Q, torch.float16)), 2, "dtype"),
+    (lambda a: a.__setitem__("q", _t((2, 8, 64, 512))), 1, "head dim"),
+    (lambda a: a.__setitem__("out", _t((2, 8, 63, 64))), 1, "out shape"),
+    (lambda a: a.__setitem__("q", _t(Q, strides=[8 * 64 * 128, 64 * 128, 128, 2])), 1,
+     "contiguous"),
+    (lambda a: a["q"].__setattr__("data", 0), 1, "NULL"),
+    (lambda a: a["q"].__setattr__("reserved", 3), 1, "reserved"),
+])
+def test_invalid_arguments_rejected(lib, mutate, code, needle):
+    a = {"q": _t(Q), "k": _t(KV), "v": _t(KV), "p": _p(), "out": _t(Q)}
+    mutate(a)
+    r, detail = _call(lib, a["q"], a["k"], a["v"], a["p"], a["out"])
+    assert r == code, detail
+    assert needle in detail
+
+
+def test_head_dim_256_bf16_ok_for_sizes(lib):
+    n = ctypes.c_size_t(123)
+    r = lib.attn_fwd_workspace_bytes(ctypes.byref(_t((1, 16, 8, 256))),
+                                     ctypes.byref(_t((1, 8, 8, 256))),
+                                     ctypes.byref(_t((1, 8, 8, 256))), None,
+                                     ctypes.byref(_p()), ctypes.byref(n))
+    assert r == 0 and n.value == 0
+
+
+def test_null_params_and_bytes(lib):
+    r = lib.attn_fwd(ctypes.byref(_t(Q)), ctypes.byref(_t(KV)), ctypes.byref(_t(KV)), None, None,
+                     ctypes.byref(_t(Q)), None, None, 0, None)
+    assert r == 1
+    r = lib.attn_fwd_workspace_bytes(ctypes.byref(_t(Q)), ctypes.byref(_t(KV)),
+                                     ctypes.byref(_t(KV)), None, ctypes.byref(_p()), None)
+    assert r == 1
+
+
+def _paged(bs=16, max_blocks=8, table=0x2000, lens=0x3000):
+    pd = B._Paged()
+    pd.block_table, pd.seq_lens, pd.block_size, pd.max_blocks = table, lens, bs, max_blocks
+    return pd
+
+
+def test_paged_validation(lib):
+    q = _t((4, 32, 1, 128))
+    cache = _t((100, 16, 8, 128))
+    r, d = _call(lib, q, cache, cache, _p(), paged=_paged(bs=32))
+    assert r == 1 and "block_size" in d
+    r, d = _call(lib, q, cache, cache, _p(), paged=_paged(table=0))
+    assert r == 1 and "NULL" in d
+    r, d = _call(lib, q, cache, cache, _p(), paged=_paged(max_blocks=0))
+    assert r == 1 and "max_blocks" in d
+    r, d = _call(lib, q, cache, _t((100, 16, 4, 128)), _p(), paged=_paged())
+    assert r == 1
+
+
+def test_workspace_query_needs_no_device(lib):
+    # a pure host computation: works in a process without a GPU
+    n = ctypes.c_size_t(7)
+    q = _t((4, 32, 1, 128))
+    cache = _t((100, 16, 8, 128))
+    pd = _paged(table=0, lens=0)
+    r = lib.attn_fwd_workspace_bytes(ctypes.byref(q), ctypes.byref(cache), ctypes.byref(cache),
+                                     ctypes.byref(pd), ctypes.byref(_p(norm=2)), ctypes.byref(n))
+    assert r == 0
+    assert n.value >= 0
+
+
+def test_python_wrapper_rejects_dense_mask_and_dropout():
+    q = torch.zeros(1, 2, 4, 16)
+    with pytest.raises(apn.AttnError):
+        apn.custom_attention(None, q, q, q, torch.ones(4, 4, dtype=torch.bool), normalizer="softmax")
+    with pytest.raises(apn.AttnError):
+        apn.custom_attention(None, q, q, q, None, normalizer="softmax", dropout=0.1)
+    with pytest.raises(apn.AttnError):
+        apn.custom_attention(None, q, q, q, None, normalizer="softmax", output_attentions=True)
