@@ -1,7 +1,404 @@
-// Tiled bf16 prefill kernels (matrix cores).  Placeholder until implemented.
+// Tiled bf16 prefill on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// One workgroup owns BM = 32 * NW query rows of one (batch, query head); each
+// wave owns 32 rows.  K/V tiles of BN keys stream through LDS (double
+// buffered), shared by the waves.  Per tile and wave:
+//
+//   S^T (keys x queries) = K_tile . Q^T      A = K rows (LDS), B = Q (registers)
+//   O^T (d x queries)   += V_tile^T . P^T    A = V^T (LDS),   B = P (registers)
+//
+// Computing the transposed products puts one query in each lane (lanes l and
+// l+32 share query l%32 and hold complementary halves of its keys), so the
+// row reductions of the normalizer are in-lane plus one exchange with the
+// partner lane, and the probabilities P leave the S accumulators already in
+// the register layout the PV product consumes.  The contraction of the PV
+// product runs over keys, so V is transposed while it is staged into LDS.
+//
+// Masking is computed, never stored: the workgroup visits only key tiles
+// inside its causal / window bounds ("Attention variants": a kernel that
+// skips blocks outside the window), a wave skips tiles its own 32 rows
+// cannot see, and the per-element test runs only on tiles that straddle a
+// bound.
+//
+// Normalizers: softmax and softmax1 use the online (running max, running
+// sum) update; for softmax1 the "+1" enters as a virtual key with logit 0
+// and value 0, i.e. the running max starts at 0 and the running sum at 1
+// ("HF Attention Normalizers", "Important Limitations").
+
 #include "common.h"
 
 namespace attn {
-bool prefill_mfma_supported(const FwdArgs&) { return false; }
-hipError_t launch_prefill_mfma(const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D_, int BN_, int NW_>
+struct Cfg {
+  static constexpr int D = D_, BN = BN_, NW = NW_;
+  static constexpr int NT = NW * 64;          // threads per workgroup
+  static constexpr int BM = NW * 32;          // query rows per workgroup
+  static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
+  static constexpr int KCH = BN * CPR;        // chunks per K tile
+  static constexpr int KPT = KCH / NT;        // K chunks per thread
+  static constexpr int VUN = (BN / 4) * CPR;  // V staging units (4 keys x 8 dims)
+  static constexpr int VPT = (VUN + NT - 1) / NT;
+  static constexpr int NKB = BN / 32;         // 32-key blocks per tile
+  static constexpr int NDB = D / 32;          // 32-dim blocks of the output
+  static constexpr int NQC = D / 16;          // 16-dim steps of QK^T
+  static constexpr int VSW = (BN / 8 >= 8) ? 7 : (BN / 8 - 1);  // V^T chunk swizzle mask
+  static_assert(KCH % NT == 0, "K tile must split evenly over the threads");
+  static_assert(CPR >= 8, "head dim must be >= 64");
+  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
+
+// Position of tile key kk inside a V^T row.  Within each group of 16 keys the
+// order is 0-3, 8-11, 4-7, 12-15: the 8 keys one lane half feeds to a PV
+// step are then contiguous (see the S^T accumulator layout).
+__device__ __forceinline__ int vt_pos(int kk) {
+  const int q = (kk >> 2) & 3;  // which group of 4 inside the 16
+  const int sw = (q == 1) ? 2 : (q == 2 ? 1 : q);
+  return (kk & ~15) | (sw << 2) | (kk & 3);
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS row (spreads the 32 rows a
+// wave reads at one column over distinct banks).
+__device__ __forceinline__ int k_chunk(int row, int ch) { return ch ^ (row & 7); }
+template <int VSW>
+__device__ __forceinline__ int v_chunk(int d, int ch) { return ch ^ ((d ^ (d >> 3)) & VSW); }
+
+struct RowBounds {
+  int lo, hi;  // visible keys [lo, hi) of one query row
+};
+
+__device__ __forceinline__ RowBounds row_bounds(int q, int Lq, int Lk, int causal, int window) {
+  RowBounds r;
+  const int qp = q + Lk - Lq;
+  int hi = causal ? min(Lk, qp + 1) : Lk;
+  hi = max(hi, 0);
+  int lo = window ? max(0, qp - window + 1) : 0;
+  r.lo = min(lo, hi);
+  r.hi = hi;
+  return r;
+}
+
+// Maps the hardware workgroup id to (batch*head, q-block).  Workgroups are
+// dealt round-robin to the 8 XCDs; renumbering gives every XCD a contiguous
+// range of (batch, head) pairs, so the query heads sharing one K/V head stay
+// in one L2, and within a pair the longest (last) q-blocks start first.
+__device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
+  const int nblk = gridDim.x;
+  int id = blockIdx.x;
+  if ((nblk & 7) == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
+  bh = id / nqb;
+  qb = nqb - 1 - (id - bh * nqb);
+}
+
+template <class C>
+struct Tiles {
+  // global -> registers
+  u32x4 kr[C::KPT];
+  u32x4 vr[C::VPT][4];
+
+  __device__ __forceinline__ void load(const bf16_t* kb, const bf16_t* vb, int64_t ksl,
+                                       int64_t vsl, int k0, int Lk, int tid) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int id = tid + i * C::NT;
+      const int row = id / C::CPR, ch = id % C::CPR;
+      const int key = k0 + row;
+      kr[i] = key < Lk ? *(const u32x4*)(kb + (int64_t)key * ksl + ch * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int id = tid + i * C::NT;
+      if (C::VUN % C::NT == 0 || id < C::VUN) {
+        const int kg = id / C::CPR, ch = id % C::CPR;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + kg * 4 + j;
+          vr[i][j] = key < Lk ? *(const u32x4*)(vb + (int64_t)key * vsl + ch * 8)
+                              : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+
+  // registers -> LDS (K row-major, V transposed)
+  __device__ __forceinline__ void store(bf16_t* kl, bf16_t* vl, int tid) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int id = tid + i * C::NT;
+      const int row = id / C::CPR, ch = id % C::CPR;
+      *(u32x4*)(kl + row * C::D + k_chunk(row, ch) * 8) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int id = tid + i * C::NT;
+      if (C::VUN % C::NT == 0 || id < C::VUN) {
+        const int kg = id / C::CPR, ch = id % C::CPR;
+        const int pos = vt_pos(kg * 4);
+        const int pch = pos >> 3, poff = pos & 7;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // dword w of each key row = dims 2w, 2w+1
+          const unsigned a0 = vr[i][0][w], a1 = vr[i][1][w], a2 = vr[i][2][w], a3 = vr[i][3][w];
+#pragma unroll
+          for (int hbit = 0; hbit < 2; ++hbit) {
+            const int d = ch * 8 + 2 * w + hbit;
+            u32x2 val;
+            if (hbit == 0) {
+              val[0] = (a0 & 0xffffu) | (a1 << 16);
+              val[1] = (a2 & 0xffffu) | (a3 << 16);
+            } else {
+              val[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+              val[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+            }
+            *(u32x2*)(vl + d * C::BN + v_chunk<C::VSW>(d, pch) * 8 + poff) = val;
+          }
+        }
+      }
+    }
+  }
+};
+
+// S^T accumulators of one tile for this wave: s[kb][r] is the raw q.k of key
+// k0 + 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 and query lane % 32.
+template <class C>
+__device__ __forceinline__ void qk_tile(const bf16_t* kl, const bf16x8* qreg, int l32, int g,
+                                        f32x16* s) {
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < C::NQC; ++c) {
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      const int row = kb * 32 + l32;
+      const bf16x8 kv = *(const bf16x8*)(kl + row * C::D + k_chunk(row, 2 * c + g) * 8);
+      s[kb] = mfma(kv, qreg[c], s[kb]);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void pv_tile(const bf16_t* vl, const bf16x8* pk, int l32, int g,
+                                        f32x16* o) {
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    const int d = db * 32 + l32;
+#pragma unroll
+    for (int t = 0; t < 2 * C::NKB; ++t) {
+      const bf16x8 vv = *(const bf16x8*)(vl + d * C::BN + v_chunk<C::VSW>(d, 2 * t + g) * 8);
+      o[db] = mfma(vv, pk[t], o[db]);
+    }
+  }
+}
+
+__device__ __forceinline__ int s_key(int k0, int kb, int r, int g) {
+  return k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+}
+
+// logit softcap in the log2 domain: log2(e) * cap * tanh(raw * scaling / cap)
+__device__ __forceinline__ float capped_log2(float raw, float sc_over_cap, float cap_log2e) {
+  const float y = raw * sc_over_cap;
+  const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);  // exp(2y)
+  const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);  // tanh(y)
+  return cap_log2e * t;
+}
+
+template <class C, int NORM, bool CAP>
+__global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * C::BN * C::D];
+  bf16_t* const kl0 = lds;
+  bf16_t* const vl0 = lds + 2 * C::BN * C::D;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int Lq = a.Lq, Lk = a.Lk;
+  const int nqb = (Lq + C::BM - 1) / C::BM;
+  int bh, qb;
+  block_coords(nqb, bh, qb);
+  const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
+  const int q0 = qb * C::BM;
+
+  const bf16_t* qbase = (const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+  const bf16_t* vbase = (const bf16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+
+  // key tiles the workgroup visits
+  const int qlast = min(q0 + C::BM, Lq) - 1;
+  const RowBounds first = row_bounds(q0, Lq, Lk, a.causal, a.window);
+  const RowBounds last = row_bounds(qlast, Lq, Lk, a.causal, a.window);
+  const int klo = first.lo, khi = last.hi;
+  const int t0 = klo / C::BN;
+  const int t1 = khi > klo ? (khi + C::BN - 1) / C::BN : t0;
+
+  // this wave's rows and this lane's row
+  const int wq0 = q0 + 32 * wave;
+  const int wq1 = min(wq0 + 31, Lq - 1);
+  const bool wave_rows = wq0 < Lq;
+  const RowBounds wfirst = row_bounds(wq0, Lq, Lk, a.causal, a.window);
+  const RowBounds wlast = row_bounds(wq1, Lq, Lk, a.causal, a.window);
+  const int myq = wq0 + l32;
+  const bool row_ok = myq < Lq;
+  const RowBounds mine = row_bounds(row_ok ? myq : wq1, Lq, Lk, a.causal, a.window);
+
+  bf16x8 qreg[C::NQC];
+  {
+    const bf16_t* qrow = qbase + (int64_t)myq * a.q_sl;
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c)
+      qreg[c] = row_ok ? *(const bf16x8*)(qrow + 16 * c + 8 * g) : bf16x8{};
+  }
+
+  f32x16 o[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
+  float m2 = (NORM == ATTN_SOFTMAX1) ? 0.f : -INFINITY;  // running max, log2 units
+  float lsum = (NORM == ATTN_SOFTMAX1 && g == 0) ? 1.f : 0.f;
+  const float c2 = a.scaling * kLog2e;
+  const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
+  const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;
+
+  Tiles<C> tiles;
+  if (t0 < t1) {
+    tiles.load(kbase, vbase, a.k_sl, a.v_sl, t0 * C::BN, Lk, tid);
+    tiles.store(kl0, vl0, tid);
+  }
+  __syncthreads();
+
+  for (int t = t0; t < t1; ++t) {
+    const int cur = (t - t0) & 1;
+    const bf16_t* kl = kl0 + cur * C::BN * C::D;
+    const bf16_t* vl = vl0 + cur * C::BN * C::D;
+    if (t + 1 < t1) tiles.load(kbase, vbase, a.k_sl, a.v_sl, (t + 1) * C::BN, Lk, tid);
+    const int k0 = t * C::BN;
+    const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+    if (active) {
+      f32x16 s[C::NKB];
+      qk_tile<C>(kl, qreg, l32, g, s);
+      const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+      // scores to the log2 domain (softcap), masking, tile max
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r];
+          if (CAP) x = capped_log2(x, sc_over_cap, cap_log2e);
+          if (edge) {
+            const int key = s_key(k0, kb, r, g);
+            if (key < mine.lo || key >= mine.hi) x = -INFINITY;
+          }
+          s[kb][r] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+      mt = fmaxf(mt, partner(mt));
+      const float mt2 = CAP ? mt : mt * c2;
+      const float m_new = fmaxf(m2, mt2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
+      m2 = m_new;
+      float ps = 0.f;
+      bf16x8 pk[2 * C::NKB];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - m_use)
+                              : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_use));
+          ps += p;
+          pk[2 * kb + (r >> 3)][r & 7] = (bf16_t)p;
+        }
+      }
+      lsum = fmaf(lsum, alpha, ps);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+      pv_tile<C>(vl, pk, l32, g, o);
+    }
+    if (t + 1 < t1) {
+      bf16_t* kln = kl0 + (cur ^ 1) * C::BN * C::D;
+      bf16_t* vln = vl0 + (cur ^ 1) * C::BN * C::D;
+      tiles.store(kln, vln, tid);
+    }
+    __syncthreads();
+  }
+
+  // epilogue
+  const float ltot = lsum + partner(lsum);
+  if (row_ok) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(o[db][4 * rq + e] * inv);
+        *(bf16x4*)(orow + db * 32 + 8 * rq + 4 * g) = w;
+      }
+    }
+    if (a.stats && g == 0) {
+      float* st = a.stats + (((int64_t)b * a.Hq + h) * Lq + myq) * 2;
+      st[0] = m2 == -INFINITY ? -INFINITY : m2 * (1.f / kLog2e);
+      st[1] = ltot;
+    }
+  }
+}
+
+template <class C, int NORM>
+hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.Lq + C::BM - 1) / C::BM;
+  dim3 grid((unsigned)(nqb * a.B * a.Hq)), block(C::NT);
+  if (a.softcap > 0.f)
+    prefill_softmax_kernel<C, NORM, true><<<grid, block, 0, stream>>>(a);
+  else
+    prefill_softmax_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int NORM>
+hipError_t launch_norm(const FwdArgs& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_cfg<Cfg<64, 64, 4>, NORM>(a, stream);
+    case 128: return launch_cfg<Cfg<128, 64, 4>, NORM>(a, stream);
+    default: return launch_cfg<Cfg<256, 32, 4>, NORM>(a, stream);
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+bool prefill_mfma_supported(const FwdArgs& a) {
+  if (a.dtype != ATTN_BF16 || a.paged) return false;
+  if (a.D != 64 && a.D != 128 && a.D != 256) return false;
+  if (a.norm != ATTN_SOFTMAX && a.norm != ATTN_SOFTMAX1) return false;
+  if (!(a.scaling > 0.f)) return false;
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.out)) return false;
+  const int64_t s[] = {a.q_sb, a.q_sh, a.q_sl, a.k_sb, a.k_sh, a.k_sl,
+                       a.v_sb, a.v_sh, a.v_sl, a.o_sb, a.o_sh, a.o_sl};
+  for (int64_t x : s)
+    if (x % 8) return false;
+  const int nqb_min = (a.Lq + 127) / 128;
+  return (int64_t)nqb_min * a.B * a.Hq <= (int64_t)INT32_MAX;
+}
+
+hipError_t launch_prefill_mfma(const FwdArgs& a, hipStream_t stream) {
+  return a.norm == ATTN_SOFTMAX1 ? launch_norm<ATTN_SOFTMAX1>(a, stream)
+                                 : launch_norm<ATTN_SOFTMAX>(a, stream);
+}
+
 }  // namespace attn
