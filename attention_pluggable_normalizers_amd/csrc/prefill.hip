@@ -111,8 +111,7 @@ struct Tiles {
   u32x4 kr[C::KPT];
   u32x4 vr[C::VPT][4];
 
-  __device__ __forceinline__ void load(const bf16_t* kb, const bf16_t* vb, int64_t ksl,
-                                       int64_t vsl, int k0, int Lk, int tid) {
+  __device__ __forceinline__ void load_k(const bf16_t* kb, int64_t ksl, int k0, int Lk, int tid) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int id = tid + i * C::NT;
@@ -120,6 +119,9 @@ struct Tiles {
       const int key = k0 + row;
       kr[i] = key < Lk ? *(const u32x4*)(kb + (int64_t)key * ksl + ch * 8) : u32x4{0, 0, 0, 0};
     }
+  }
+
+  __device__ __forceinline__ void load_v(const bf16_t* vb, int64_t vsl, int k0, int Lk, int tid) {
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
       const int id = tid + i * C::NT;
@@ -135,14 +137,24 @@ struct Tiles {
     }
   }
 
-  // registers -> LDS (K row-major, V transposed)
-  __device__ __forceinline__ void store(bf16_t* kl, bf16_t* vl, int tid) {
+  __device__ __forceinline__ void load(const bf16_t* kb, const bf16_t* vb, int64_t ksl,
+                                       int64_t vsl, int k0, int Lk, int tid) {
+    load_k(kb, ksl, k0, Lk, tid);
+    load_v(vb, vsl, k0, Lk, tid);
+  }
+
+  // registers -> LDS, K row-major
+  __device__ __forceinline__ void store_k(bf16_t* kl, int tid) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int id = tid + i * C::NT;
       const int row = id / C::CPR, ch = id % C::CPR;
       *(u32x4*)(kl + row * C::D + k_chunk(row, ch) * 8) = kr[i];
     }
+  }
+
+  // registers -> LDS, V transposed
+  __device__ __forceinline__ void store_v(bf16_t* vl, int tid) {
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
       const int id = tid + i * C::NT;
@@ -169,6 +181,11 @@ struct Tiles {
         }
       }
     }
+  }
+
+  __device__ __forceinline__ void store(bf16_t* kl, bf16_t* vl, int tid) {
+    store_k(kl, tid);
+    store_v(vl, tid);
   }
 };
 
@@ -265,7 +282,11 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
   float m2 = (NORM == ATTN_SOFTMAX1) ? 0.f : -INFINITY;  // running max, log2 units
+  // running sums of the weights: exact (for row_stats) and of the bf16-rounded
+  // weights the PV product actually uses (the output is normalized by the
+  // latter, which cancels most of the rounding of P)
   float lsum = (NORM == ATTN_SOFTMAX1 && g == 0) ? 1.f : 0.f;
+  float lrnd = lsum;
   const float c2 = a.scaling * kLog2e;
   const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
   const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
       m2 = m_new;
-      float ps = 0.f;
+      float ps = 0.f, psr = 0.f;
       bf16x8 pk[2 * C::NKB];
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
@@ -318,11 +339,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
         for (int r = 0; r < 16; ++r) {
           const float p = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - m_use)
                               : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_use));
+          const bf16_t pb = (bf16_t)p;
           ps += p;
-          pk[2 * kb + (r >> 3)][r & 7] = (bf16_t)p;
+          psr += (float)pb;
+          pk[2 * kb + (r >> 3)][r & 7] = pb;
         }
       }
       lsum = fmaf(lsum, alpha, ps);
+      lrnd = fmaf(lrnd, alpha, psr);
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
       pv_tile<C>(vl, pk, l32, g, o);
@@ -337,8 +361,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 
   // epilogue
   const float ltot = lsum + partner(lsum);
+  const float lrtot = lrnd + partner(lrnd);
   if (row_ok) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float inv = lrtot > 0.f ? 1.f / lrtot : 0.f;
     bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -358,14 +383,451 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   }
 }
 
+// ---------------------------------------------------------------------------
+// sparsemax and 1.5-entmax
+//
+// p = g(z - tau) with g(x) = max(x, 0) (sparsemax, z = s) or max(x, 0)^2
+// (1.5-entmax, z = s / 2), tau fixed per row by sum_j g(z_j - tau) = 1
+// ("HF Attention Normalizers", "Supported Normalizers"; "Important
+// Limitations": stream K tiles, find one threshold per query row, then
+// recompute the tiles for the weighted sum of V).
+//
+// Pass A streams the K tiles once.  Each row keeps a provable lower bound
+// `floor` <= tau and, in LDS, every score seen so far that lies above it (the
+// candidates; each lane keeps its own half of the row).  Valid lower bounds:
+// max z - 1 (the top key alone already has weight 1 there), and the threshold
+// of any subset of the row's scores (adding scores can only raise tau), which
+// Michelot's step (sparsemax) or a Newton step from the left (1.5-entmax; g
+// is convex) approaches from below.  When a lane's buffer fills, the row
+// raises its floor by such steps over its candidates and drops those at or
+// below it.  After the pass the candidates contain the support, and tau is
+// the closed form over the candidate set once that value lies below every
+// remaining candidate (then the set is exactly the support):
+//   sparsemax: tau = (sum z - 1) / k
+//   1.5-entmax: tau = mean - sqrt((1 - sum (z - mean)^2) / k).
+// A row whose support does not fit its buffer is finished by extra passes
+// over the K tiles that accumulate (count, sum, sum of squares, minimum)
+// above its floor and step the floor until the closed form is consistent.
+// Pass B recomputes the scores with the same instruction sequence (so every
+// z is bit-identical) and accumulates g(z - tau) V; the weights already sum
+// to one.
+// ---------------------------------------------------------------------------
+
+template <class C>
+struct SparseCfg {
+  static constexpr int REGION_BYTES = 65536 - 2 * C::BN * C::D * 2;  // V tiles / candidates
+  static constexpr int SCAP = REGION_BYTES / (C::NT * 4);            // candidates per lane
+  static_assert(REGION_BYTES >= 2 * C::BN * C::D * 2, "region must hold two V tiles");
+  static_assert(SCAP >= 17, "candidate buffer too small");
+};
+
+// z of one raw score q.k (the value the threshold acts on).
+template <bool CAP>
+__device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, float capz) {
+#pragma clang fp contract(off)
+  if (CAP) {
+    const float y = raw * sc_over_cap;
+    const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
+    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
+    return capz * t;
+  }
+  return raw * cz;
+}
+
+__device__ __forceinline__ double partner_d(double x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ int partner_i(int x) { return __shfl_xor(x, 32, 64); }
+
+// One step of the threshold search from lower bound t over the candidate set
+// L = {z > t} with row totals (count c, sum and sum of squares of z - mref,
+// smallest member mn).  Sets `exact` and returns tau when the closed form
+// over L is consistent; otherwise returns a larger lower bound that drops at
+// least the smallest member of L.
+template <int NORM>
+__device__ __forceinline__ double thr_step(double c, double s1, double s2, float mn, double mref,
+                                           double t, bool& exact) {
+  const double ty = t - mref;
+  double tcf, step;
+  bool valid;
+  if (NORM == ATTN_SPARSEMAX) {
+    tcf = (s1 - 1.0) / c;
+    valid = true;
+    step = tcf;
+  } else {
+    const double mu = s1 / c;
+    const double ss = s2 - s1 * mu;
+    const double delta = (1.0 - ss) / c;
+    valid = delta >= 0.0;
+    tcf = valid ? mu - sqrt(delta) : 0.0;
+    const double f = s2 - 2.0 * ty * s1 + c * ty * ty - 1.0;
+    const double fp = 2.0 * (s1 - c * ty);
+    step = ty + f / fp;
+  }
+  const double mny = (double)mn - mref;
+  if (valid && tcf < mny) {
+    exact = true;
+    return mref + tcf;
+  }
+  exact = false;
+  return mref + fmax(step, mny);
+}
+
+// Largest float not above x.
+__device__ __forceinline__ float float_floor(double x) {
+  float f = (float)x;
+  if ((double)f > x) {  // step one ulp towards -inf
+    unsigned u = __float_as_uint(f);
+    u = f > 0.f ? u - 1u : (f < 0.f ? u + 1u : 0x80000001u);
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+
+// Keeps this lane's candidates above t (compacting them) and returns their
+// partial sums of y = z - mref.
+template <int SCAP>
+__device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double mref, double& c,
+                                         double& s1, double& s2, float& mn) {
+  int w = 0;
+  c = s1 = s2 = 0.0;
+  mn = INFINITY;
+  for (int e = 0; e < cnt; ++e) {
+    const float z = buf[e * 64];
+    if ((double)z > t) {
+      buf[w * 64] = z;
+      ++w;
+      const double y = (double)z - mref;
+      c += 1.0;
+      s1 += y;
+      s2 += y * y;
+      mn = fminf(mn, z);
+    }
+  }
+  cnt = w;
+}
+
+template <class C, int NORM, bool CAP>
+__global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_kernel(FwdArgs a) {
+  using SC = SparseCfg<C>;
+  constexpr int SCAP = SC::SCAP;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BN * C::D + SC::REGION_BYTES / 2];
+  bf16_t* const kl0 = lds;
+  bf16_t* const vl0 = lds + 2 * C::BN * C::D;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int Lq = a.Lq, Lk = a.Lk;
+  const int nqb = (Lq + C::BM - 1) / C::BM;
+  int bh, qb;
+  block_coords(nqb, bh, qb);
+  const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
+  const int q0 = qb * C::BM;
+
+  const bf16_t* qbase = (const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+  const bf16_t* vbase = (const bf16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+
+  const int qlast = min(q0 + C::BM, Lq) - 1;
+  const RowBounds first = row_bounds(q0, Lq, Lk, a.causal, a.window);
+  const RowBounds last = row_bounds(qlast, Lq, Lk, a.causal, a.window);
+  const int klo = first.lo, khi = last.hi;
+  const int t0 = klo / C::BN;
+  const int t1 = khi > klo ? (khi + C::BN - 1) / C::BN : t0;
+
+  const int wq0 = q0 + 32 * wave;
+  const int wq1 = min(wq0 + 31, Lq - 1);
+  const bool wave_rows = wq0 < Lq;
+  const RowBounds wfirst = row_bounds(wq0, Lq, Lk, a.causal, a.window);
+  const RowBounds wlast = row_bounds(wq1, Lq, Lk, a.causal, a.window);
+  const int myq = wq0 + l32;
+  const bool row_ok = myq < Lq;
+  const RowBounds mine = row_bounds(row_ok ? myq : wq1, Lq, Lk, a.causal, a.window);
+
+  bf16x8 qreg[C::NQC];
+  {
+    const bf16_t* qrow = qbase + (int64_t)myq * a.q_sl;
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c)
+      qreg[c] = row_ok ? *(const bf16x8*)(qrow + 16 * c + 8 * g) : bf16x8{};
+  }
+
+  const bool ent = (NORM == ATTN_ENTMAX15);
+  const float cz = ent ? 0.5f * a.scaling : a.scaling;
+  const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
+  const float capz = CAP ? (ent ? 0.5f * a.softcap : a.softcap) : 0.f;
+
+  // ---- pass A: row max, floor and candidates --------------------------------
+  float* const buf = (float*)vl0 + wave * SCAP * 64 + lane;
+  float mrun = -INFINITY;     // running max of z over the row (both lanes)
+  double floor_ = -INFINITY;  // lower bound on tau (z units)
+  float floor_f = -INFINITY;  // largest float <= floor_
+  int cnt = 0;                // this lane's candidates
+  bool ovf = !row_ok;         // row left to the extra passes (or no row at all)
+
+  auto refloor = [&]() __attribute__((always_inline)) {
+    // wave-uniform: every lane takes part (partner exchanges inside)
+    for (int it = 0; it < 8; ++it) {
+      double c, s1, s2;
+      float mn;
+      scan_buf<SCAP>(buf, cnt, floor_, (double)mrun, c, s1, s2, mn);
+      c += partner_d(c);
+      s1 += partner_d(s1);
+      s2 += partner_d(s2);
+      mn = fminf(mn, partner(mn));
+      if (!ovf && c > 0.0) {
+        bool ex;
+        const double tn = thr_step<NORM>(c, s1, s2, mn, (double)mrun, floor_, ex);
+        floor_ = fmax(floor_, tn);
+        floor_f = float_floor(floor_);
+      }
+      const int pc = partner_i(cnt);
+      const bool need = !ovf && (cnt + 16 > SCAP || pc + 16 > SCAP);
+      if (!__any(need)) break;
+    }
+    const int pc = partner_i(cnt);
+    if (cnt + 16 > SCAP || pc + 16 > SCAP) ovf = true;
+  };
+
+  Tiles<C> tiles;
+  if (t0 < t1) {
+    tiles.load_k(kbase, a.k_sl, t0 * C::BN, Lk, tid);
+    tiles.store_k(kl0, tid);
+  }
+  __syncthreads();
+  for (int t = t0; t < t1; ++t) {
+    const int cur = (t - t0) & 1;
+    const bf16_t* kl = kl0 + cur * C::BN * C::D;
+    if (t + 1 < t1) tiles.load_k(kbase, a.k_sl, (t + 1) * C::BN, Lk, tid);
+    const int k0 = t * C::BN;
+    const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+    if (active) {
+      f32x16 s[C::NKB];
+      qk_tile<C>(kl, qreg, l32, g, s);
+      const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float z = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
+          if (edge) {
+            const int key = s_key(k0, kb, r, g);
+            if (key < mine.lo || key >= mine.hi) z = -INFINITY;
+          }
+          s[kb][r] = z;
+          mt = fmaxf(mt, z);
+        }
+      }
+      mt = fmaxf(mt, partner(mt));
+      if (mt > mrun) {
+        mrun = mt;
+        const double fl = (double)mrun - 1.0;
+        if (fl > floor_) {
+          floor_ = fl;
+          floor_f = float_floor(floor_);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) any |= s[kb][r] > floor_f;
+        if (__any(any && !ovf)) {
+          if (__any(!ovf && cnt + 16 > SCAP)) refloor();
+          if (!ovf) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float z = s[kb][r];
+              if (z > floor_f) {
+                buf[cnt * 64] = z;
+                ++cnt;
+              }
+            }
+          }
+        }
+      }
+    }
+    if (t + 1 < t1) tiles.store_k(kl0 + (cur ^ 1) * C::BN * C::D, tid);
+    __syncthreads();
+  }
+
+  // ---- exact threshold over the candidates ---------------------------------
+  double tau = INFINITY;
+  int ksup = 0;
+  bool done = !row_ok || mrun == -INFINITY || ovf;  // empty rows: tau = +inf, k = 0
+  bool pending = row_ok && mrun != -INFINITY && ovf;  // left to the extra passes
+  for (int it = 0; it < 2 * SCAP + 4; ++it) {
+    if (!__any(!done)) break;
+    double c, s1, s2;
+    float mn;
+    scan_buf<SCAP>(buf, cnt, floor_, (double)mrun, c, s1, s2, mn);
+    c += partner_d(c);
+    s1 += partner_d(s1);
+    s2 += partner_d(s2);
+    mn = fminf(mn, partner(mn));
+    if (!done) {
+      bool ex;
+      const double tn = thr_step<NORM>(c, s1, s2, mn, (double)mrun, floor_, ex);
+      if (ex) {
+        tau = tn;
+        ksup = (int)c;
+        done = true;
+      } else {
+        floor_ = fmax(floor_, tn);
+      }
+    }
+  }
+  if (!done) pending = true;  // cannot happen (each step drops a candidate); kept as a guard
+
+  // ---- extra passes for rows whose support outgrew the buffer --------------
+  while (__syncthreads_or(pending)) {
+    double c = 0.0, s1 = 0.0, s2 = 0.0;
+    float mn = INFINITY;
+    const double mref = (double)mrun;
+    if (t0 < t1) {
+      tiles.load_k(kbase, a.k_sl, t0 * C::BN, Lk, tid);
+      tiles.store_k(kl0, tid);
+    }
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+      const int cur = (t - t0) & 1;
+      const bf16_t* kl = kl0 + cur * C::BN * C::D;
+      if (t + 1 < t1) tiles.load_k(kbase, a.k_sl, (t + 1) * C::BN, Lk, tid);
+      const int k0 = t * C::BN;
+      const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(pending);
+      if (active) {
+        f32x16 s[C::NKB];
+        qk_tile<C>(kl, qreg, l32, g, s);
+        const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+        if (pending) {
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float z = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
+              if (edge) {
+                const int key = s_key(k0, kb, r, g);
+                if (key < mine.lo || key >= mine.hi) z = -INFINITY;
+              }
+              if ((double)z > floor_) {
+                const double y = (double)z - mref;
+                c += 1.0;
+                s1 += y;
+                s2 += y * y;
+                mn = fminf(mn, z);
+              }
+            }
+          }
+        }
+      }
+      if (t + 1 < t1) tiles.store_k(kl0 + (cur ^ 1) * C::BN * C::D, tid);
+      __syncthreads();
+    }
+    c += partner_d(c);
+    s1 += partner_d(s1);
+    s2 += partner_d(s2);
+    mn = fminf(mn, partner(mn));
+    if (pending) {
+      bool ex;
+      const double tn = thr_step<NORM>(c, s1, s2, mn, mref, floor_, ex);
+      if (ex) {
+        tau = tn;
+        ksup = (int)c;
+        pending = false;
+      } else {
+        floor_ = fmax(floor_, tn);
+      }
+    }
+  }
+
+  // ---- pass B: weighted sum of V ------------------------------------------------
+  const float tauf = (float)tau;
+  // the weights sum to one; the output is divided by the sum of their
+  // bf16-rounded values, which cancels most of the rounding of P
+  float wsum = 0.f;
+  f32x16 o[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
+  if (t0 < t1) {
+    tiles.load(kbase, vbase, a.k_sl, a.v_sl, t0 * C::BN, Lk, tid);
+    tiles.store(kl0, vl0, tid);
+  }
+  __syncthreads();
+  for (int t = t0; t < t1; ++t) {
+    const int cur = (t - t0) & 1;
+    const bf16_t* kl = kl0 + cur * C::BN * C::D;
+    const bf16_t* vl = vl0 + cur * C::BN * C::D;
+    if (t + 1 < t1) tiles.load(kbase, vbase, a.k_sl, a.v_sl, (t + 1) * C::BN, Lk, tid);
+    const int k0 = t * C::BN;
+    const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+    if (active) {
+      f32x16 s[C::NKB];
+      qk_tile<C>(kl, qreg, l32, g, s);
+      const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+      bf16x8 pk[2 * C::NKB];
+      bool any = false;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+#pragma clang fp contract(off)
+          float z = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
+          if (edge) {
+            const int key = s_key(k0, kb, r, g);
+            if (key < mine.lo || key >= mine.hi) z = -INFINITY;
+          }
+          const float d = z - tauf;
+          float p = d > 0.f ? d : 0.f;
+          if (ent) p = p * p;
+          any |= p > 0.f;
+          const bf16_t pb = (bf16_t)p;
+          wsum += (float)pb;
+          pk[2 * kb + (r >> 3)][r & 7] = pb;
+        }
+      }
+      if (__any(any)) pv_tile<C>(vl, pk, l32, g, o);
+    }
+    if (t + 1 < t1) tiles.store(kl0 + (cur ^ 1) * C::BN * C::D, vl0 + (cur ^ 1) * C::BN * C::D, tid);
+    __syncthreads();
+  }
+
+  const float wtot = wsum + partner(wsum);
+  if (row_ok) {
+    const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
+    bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(o[db][4 * rq + e] * inv);
+        *(bf16x4*)(orow + db * 32 + 8 * rq + 4 * g) = w;
+      }
+    }
+    if (a.stats && g == 0) {
+      float* st = a.stats + (((int64_t)b * a.Hq + h) * Lq + myq) * 2;
+      st[0] = (float)tau;
+      st[1] = (float)ksup;
+    }
+  }
+}
+
 template <class C, int NORM>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.Lq + C::BM - 1) / C::BM;
   dim3 grid((unsigned)(nqb * a.B * a.Hq)), block(C::NT);
-  if (a.softcap > 0.f)
-    prefill_softmax_kernel<C, NORM, true><<<grid, block, 0, stream>>>(a);
-  else
-    prefill_softmax_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
+  const bool cap = a.softcap > 0.f;
+  if constexpr (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
+    if (cap)
+      prefill_sparse_kernel<C, NORM, true><<<grid, block, 0, stream>>>(a);
+    else
+      prefill_sparse_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (cap)
+      prefill_softmax_kernel<C, NORM, true><<<grid, block, 0, stream>>>(a);
+    else
+      prefill_softmax_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -385,7 +847,6 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 bool prefill_mfma_supported(const FwdArgs& a) {
   if (a.dtype != ATTN_BF16 || a.paged) return false;
   if (a.D != 64 && a.D != 128 && a.D != 256) return false;
-  if (a.norm != ATTN_SOFTMAX && a.norm != ATTN_SOFTMAX1) return false;
   if (!(a.scaling > 0.f)) return false;
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.out)) return false;
   const int64_t s[] = {a.q_sb, a.q_sh, a.q_sl, a.k_sb, a.k_sh, a.k_sl,
@@ -397,8 +858,12 @@ bool prefill_mfma_supported(const FwdArgs& a) {
 }
 
 hipError_t launch_prefill_mfma(const FwdArgs& a, hipStream_t stream) {
-  return a.norm == ATTN_SOFTMAX1 ? launch_norm<ATTN_SOFTMAX1>(a, stream)
-                                 : launch_norm<ATTN_SOFTMAX>(a, stream);
+  switch (a.norm) {
+    case ATTN_SOFTMAX: return launch_norm<ATTN_SOFTMAX>(a, stream);
+    case ATTN_SOFTMAX1: return launch_norm<ATTN_SOFTMAX1>(a, stream);
+    case ATTN_SPARSEMAX: return launch_norm<ATTN_SPARSEMAX>(a, stream);
+    default: return launch_norm<ATTN_ENTMAX15>(a, stream);
+  }
 }
 
 }  // namespace attn

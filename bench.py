@@ -1,0 +1,204 @@
+"""Throughput of the attention forward with pluggable normalizers on one MI355X.
+
+One step = one forward of the Llama-3.2-1B-shaped prefill workload (B=4,
+Hq=32, Hkv=8, L=2048, head dim 64, bf16, causal, scaling 1/8) for each of the
+four normalizers (softmax, softmax1, sparsemax, 1.5-entmax) on the same
+synthetic inputs, already resident in HBM.  The metric is credited TFLOP/s:
+4 * head_dim FLOPs per unmasked (query, key) pair, the same for every
+normalizer (recomputed score passes of the sparse normalizers are not
+credited).  With --decode the paged-decode workload (64 sequences of
+1024..32768 keys, 16-token pages) is timed as well and reported in GB/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode]
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def credited_pairs(cfg):
+    """Unmasked (query, key) pairs of a prefill workload (integer count)."""
+    total = 0
+    for i in range(cfg.Lq):
+        qp = i + cfg.Lk - cfg.Lq
+        hi = max(0, min(cfg.Lk, qp + 1) if cfg.causal else cfg.Lk)
+        lo = min(max(0, qp - cfg.window + 1) if cfg.window else 0, hi)
+        total += hi - lo
+    return total * cfg.B * cfg.Hq
+
+
+def decode_bytes(x, cfg, seq_lens):
+    """Bytes the paged decode must move: live K and V rows, q, out, table, lengths."""
+    live = int(sum(seq_lens))
+    kv = live * cfg.Hkv * cfg.D * 2 * 2
+    q = cfg.B * cfg.Hq * cfg.D * 2
+    out = q
+    table = sum(x.extra["pages"]) * 4
+    return kv + q + out + table + cfg.B * 4
+
+
+def cpu_baseline(cfg, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from oracle import attention_forward
+
+    q, k, v = (x.double().numpy() for x in W.make_prefill(cfg))  # exact upcast, untimed
+    threads = torch.get_num_threads()
+    # sample: query rows spread over the sequence of one (batch, head) pair,
+    # every normalizer, until the time budget is spent
+    rng = np.random.default_rng(0)
+    rows_done = 0
+    flops = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        i = int(rng.integers(cfg.Lq))
+        b, h = int(rng.integers(cfg.B)), int(rng.integers(cfg.Hq))
+        for norm in cfg.normalizers:
+            attention_forward(q, k, v, norm, cfg.causal, cfg.window, cfg.softcap, cfg.scaling,
+                              rows=[(b, h, i)])
+        n = min(cfg.Lk, i + cfg.Lk - cfg.Lq + 1) if cfg.causal else cfg.Lk
+        flops += 4 * cfg.D * n * len(cfg.normalizers)
+        rows_done += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows x {len(cfg.normalizers)} normalizers of {cfg.name} "
+                      f"(fp64 NumPy oracle, one row per call), {dt:.1f} s on {platform.processor() or 'host'}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this forward has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_pluggable_normalizers_amd as apn
+    import workloads as W
+
+    apn.load_library()
+    dev = torch.device("cuda:0")
+    cfg = W.LLAMA
+    q, k, v = [x.to(dev) for x in W.make_prefill(cfg)]
+    out = torch.empty_like(q)
+    stats = torch.empty(*q.shape[:3], 2, dtype=torch.float32, device=dev)
+    norms = list(cfg.normalizers)
+    pairs = credited_pairs(cfg)
+    flops_per_launch = 4 * cfg.D * pairs
+
+    def launch(norm):
+        apn.attn_fwd(q, k, v, out, stats, normalizer=norm, causal=cfg.causal, window=cfg.window,
+                     softcap=cfg.softcap, scaling=cfg.scaling)
+
+    for _ in range(args.warmup):
+        for n in norms:
+            launch(n)
+    torch.cuda.synchronize()
+
+    # timed region: K steps; each launch bracketed by events on the launch stream
+    evs = {n: [] for n in norms}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for n in norms:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch(n)
+            e1.record()
+            evs[n].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_norm_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in norms}
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops_per_launch * len(norms) / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(norms, key=lambda n: per_norm_ms[n])
+    achieved = flops_per_launch / (per_norm_ms[dom] * 1e-3) / 1e12
+    result = {
+        "metric": "attention fwd TFLOP/s per normalizer + % bf16 MFMA peak; decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "L": cfg.Lq,
+                   "head_dim": cfg.D, "causal": cfg.causal, "scaling": cfg.scaling,
+                   "normalizers": norms, "credited_pairs": pairs,
+                   "credited_flop_per_launch": flops_per_launch, "parallelism": "single GPU"},
+        "per_normalizer": {n: {"us": round(per_norm_ms[n] * 1e3, 1),
+                               "TFLOP/s": round(flops_per_launch / (per_norm_ms[n] * 1e-3) / 1e12, 1),
+                               "pct_bf16_peak": round(100 * flops_per_launch /
+                                                      (per_norm_ms[n] * 1e-3) / 1e12 /
+                                                      PEAK_BF16_TFLOPS, 2)} for n in norms},
+        "roofline": {"kernel": f"prefill {dom}", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+
+    if args.decode:
+        dcfg = W.DECODE
+        x = W.make_paged(dcfg, device=dev)
+        lens = x.seq_lens.cpu().tolist()
+        paged = {"block_table": x.block_table, "seq_lens": x.seq_lens,
+                 "block_size": x.block_size, "max_blocks": x.max_blocks}
+        dout = torch.empty_like(x.q)
+        dst = torch.empty(*x.q.shape[:3], 2, dtype=torch.float32, device=dev)
+        nbytes = decode_bytes(x, dcfg, lens)
+        dres = {}
+        for n in dcfg.normalizers:
+            ws_n = apn.attn_fwd_workspace_bytes(x.q, x.k_cache, x.v_cache, normalizer=n,
+                                                causal=True, scaling=dcfg.scaling, paged=paged)
+            ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+            f = lambda: apn.attn_fwd(x.q, x.k_cache, x.v_cache, dout, dst, normalizer=n,
+                                     causal=True, scaling=dcfg.scaling, paged=paged, workspace=ws)
+            for _ in range(2):
+                f()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(max(3, args.steps)):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                f()
+                e1.record()
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ts)[len(ts) // 2]
+            dres[n] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        result["decode"] = {"workload": dcfg.name, "bytes": nbytes, "per_normalizer": dres}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
