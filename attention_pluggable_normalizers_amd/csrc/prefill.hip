@@ -112,6 +112,15 @@ struct Tiles {
   u32x4 vr[C::VPT][4];
 
   __device__ __forceinline__ void load_k(const bf16_t* kb, int64_t ksl, int k0, int Lk, int tid) {
+    if (k0 + C::BN <= Lk) {  // whole tile in range (every tile but a ragged last one)
+#pragma unroll
+      for (int i = 0; i < C::KPT; ++i) {
+        const int id = tid + i * C::NT;
+        const int row = id / C::CPR, ch = id % C::CPR;
+        kr[i] = *(const u32x4*)(kb + (int64_t)(k0 + row) * ksl + ch * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int id = tid + i * C::NT;
@@ -122,6 +131,19 @@ struct Tiles {
   }
 
   __device__ __forceinline__ void load_v(const bf16_t* vb, int64_t vsl, int k0, int Lk, int tid) {
+    if (k0 + C::BN <= Lk) {
+#pragma unroll
+      for (int i = 0; i < C::VPT; ++i) {
+        const int id = tid + i * C::NT;
+        if (C::VUN % C::NT == 0 || id < C::VUN) {
+          const int kg = id / C::CPR, ch = id % C::CPR;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            vr[i][j] = *(const u32x4*)(vb + (int64_t)(k0 + kg * 4 + j) * vsl + ch * 8);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
       const int id = tid + i * C::NT;
@@ -194,18 +216,44 @@ struct Tiles {
 template <class C>
 __device__ __forceinline__ void qk_tile(const bf16_t* kl, const bf16x8* qreg, int l32, int g,
                                         f32x16* s) {
+  // operand reads are issued in groups of QG ahead of the MFMAs that use them
+  constexpr int NOP = C::NQC * C::NKB;
+  constexpr int QG = NOP < 8 ? NOP : 8;
 #pragma unroll
   for (int kb = 0; kb < C::NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-  for (int c = 0; c < C::NQC; ++c) {
+  for (int g0 = 0; g0 < NOP; g0 += QG) {
+    bf16x8 kv[QG];
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
+    for (int j = 0; j < QG; ++j) {
+      const int c = (g0 + j) / C::NKB, kb = (g0 + j) % C::NKB;
       const int row = kb * 32 + l32;
-      const bf16x8 kv = *(const bf16x8*)(kl + row * C::D + k_chunk(row, 2 * c + g) * 8);
-      s[kb] = mfma(kv, qreg[c], s[kb]);
+      kv[j] = *(const bf16x8*)(kl + row * C::D + k_chunk(row, 2 * c + g) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < QG; ++j) {
+      const int c = (g0 + j) / C::NKB, kb = (g0 + j) % C::NKB;
+      s[kb] = mfma(kv[j], qreg[c], s[kb]);
     }
   }
 }
+
+// V^T operands of a whole tile for this lane (read before the softmax work
+// so the LDS latency hides behind it).
+template <class C>
+struct VOps {
+  static constexpr int N = C::NDB * 2 * C::NKB;
+  bf16x8 v[N];
+  __device__ __forceinline__ void read(const bf16_t* vl, int l32, int g) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int d = db * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < 2 * C::NKB; ++t)
+        v[db * 2 * C::NKB + t] = *(const bf16x8*)(vl + d * C::BN + v_chunk<C::VSW>(d, 2 * t + g) * 8);
+    }
+  }
+};
 
 template <class C>
 __device__ __forceinline__ void pv_tile(const bf16_t* vl, const bf16x8* pk, int l32, int g,
@@ -213,16 +261,51 @@ __device__ __forceinline__ void pv_tile(const bf16_t* vl, const bf16x8* pk, int 
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
     const int d = db * 32 + l32;
+    bf16x8 vv[2 * C::NKB];
 #pragma unroll
-    for (int t = 0; t < 2 * C::NKB; ++t) {
-      const bf16x8 vv = *(const bf16x8*)(vl + d * C::BN + v_chunk<C::VSW>(d, 2 * t + g) * 8);
-      o[db] = mfma(vv, pk[t], o[db]);
-    }
+    for (int t = 0; t < 2 * C::NKB; ++t)
+      vv[t] = *(const bf16x8*)(vl + d * C::BN + v_chunk<C::VSW>(d, 2 * t + g) * 8);
+#pragma unroll
+    for (int t = 0; t < 2 * C::NKB; ++t) o[db] = mfma(vv[t], pk[t], o[db]);
   }
+}
+
+template <class C>
+__device__ __forceinline__ void pv_tile_ops(const VOps<C>& vo, const bf16x8* pk, f32x16* o) {
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int t = 0; t < 2 * C::NKB; ++t) o[db] = mfma(vo.v[db * 2 * C::NKB + t], pk[t], o[db]);
 }
 
 __device__ __forceinline__ int s_key(int k0, int kb, int r, int g) {
   return k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Max / sum over the two lanes that share a query row (lanes l and l ^ 32):
+// v_permlane32_swap hands each half the other half's value.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two floats to a packed pair of bf16 (round to nearest even).
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// P operand of PV step t = 2 kb + h from the 16 S^T values of block kb.
+__device__ __forceinline__ bf16x8 p_operand(const float* p8) {
+  const u32x4 w = {pack_bf16(p8[0], p8[1]), pack_bf16(p8[2], p8[3]), pack_bf16(p8[4], p8[5]),
+                   pack_bf16(p8[6], p8[7])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // logit softcap in the log2 domain: log2(e) * cap * tanh(raw * scaling / cap)
@@ -232,6 +315,12 @@ __device__ __forceinline__ float capped_log2(float raw, float sc_over_cap, float
   const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);  // tanh(y)
   return cap_log2e * t;
 }
+
+// Lazy rescaling: the accumulators O and l are kept relative to a reference
+// max m_use that only moves when the running max exceeds it by more than
+// kRescale (log2 units), so most tiles skip the O *= alpha pass; weights
+// stay <= 2^kRescale.  The true running max is tracked for row_stats.
+constexpr float kRescale = 8.f;
 
 template <class C, int NORM, bool CAP>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_kernel(FwdArgs a) {
@@ -281,12 +370,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   f32x16 o[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
-  float m2 = (NORM == ATTN_SOFTMAX1) ? 0.f : -INFINITY;  // running max, log2 units
-  // running sums of the weights: exact (for row_stats) and of the bf16-rounded
-  // weights the PV product actually uses (the output is normalized by the
-  // latter, which cancels most of the rounding of P)
-  float lsum = (NORM == ATTN_SOFTMAX1 && g == 0) ? 1.f : 0.f;
-  float lrnd = lsum;
+  // log2-domain reference max (accumulators are relative to it) and true max
+  float m_use = (NORM == ATTN_SOFTMAX1) ? 0.f : -INFINITY;
+  float m_true = m_use;
+  float lsum = (NORM == ATTN_SOFTMAX1 && g == 0) ? 1.f : 0.f;  // the softmax1 "+1" at logit 0
   const float c2 = a.scaling * kLog2e;
   const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
   const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;
@@ -308,48 +395,65 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
     if (active) {
       f32x16 s[C::NKB];
       qk_tile<C>(kl, qreg, l32, g, s);
-      const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
-      // scores to the log2 domain (softcap), masking, tile max
+      constexpr bool kPreV = VOps<C>::N <= 8;  // V operands fit in registers across the softmax
+      VOps<C> vo;
+      if constexpr (kPreV) vo.read(vl, l32, g);
+      if (CAP) {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = capped_log2(s[kb][r], sc_over_cap, cap_log2e);
+      }
+      if ((k0 + C::BN > wfirst.hi) || (k0 < wlast.lo)) {  // tile straddles a mask bound
+        const int base = k0 + 4 * g - mine.lo;
+        const unsigned span = (unsigned)(mine.hi - mine.lo);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+            s[kb][r] = off < span ? s[kb][r] : -INFINITY;
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
+      for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r];
-          if (CAP) x = capped_log2(x, sc_over_cap, cap_log2e);
-          if (edge) {
-            const int key = s_key(k0, kb, r, g);
-            if (key < mine.lo || key >= mine.hi) x = -INFINITY;
-          }
-          s[kb][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
-      mt = fmaxf(mt, partner(mt));
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      mt = pair_max(mt);
       const float mt2 = CAP ? mt : mt * c2;
-      const float m_new = fmaxf(m2, mt2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
-      m2 = m_new;
-      float ps = 0.f, psr = 0.f;
+      m_true = fmaxf(m_true, mt2);
+      const bool need = mt2 > m_use + kRescale;
+      if (__any(need)) {
+        // lanes that do not need it keep their reference (alpha = 1); a lane
+        // whose reference is still -inf gets alpha = 0 (nothing accumulated yet)
+        const float m_new = need ? mt2 : m_use;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
+        m_use = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+      }
+      const float mref = m_use == -INFINITY ? 0.f : m_use;
+      float ps = 0.f;
       bf16x8 pk[2 * C::NKB];
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
+        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - m_use)
-                              : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_use));
-          const bf16_t pb = (bf16_t)p;
-          ps += p;
-          psr += (float)pb;
-          pk[2 * kb + (r >> 3)][r & 7] = pb;
+          p[r] = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - mref)
+                     : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -mref));
+          ps += p[r];
         }
+        pk[2 * kb] = p_operand(p);
+        pk[2 * kb + 1] = p_operand(p + 8);
       }
-      lsum = fmaf(lsum, alpha, ps);
-      lrnd = fmaf(lrnd, alpha, psr);
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
-      pv_tile<C>(vl, pk, l32, g, o);
+      lsum += ps;
+      if constexpr (kPreV)
+        pv_tile_ops<C>(vo, pk, o);
+      else
+        pv_tile<C>(vl, pk, l32, g, o);
     }
     if (t + 1 < t1) {
       bf16_t* kln = kl0 + (cur ^ 1) * C::BN * C::D;
@@ -360,25 +464,25 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   }
 
   // epilogue
-  const float ltot = lsum + partner(lsum);
-  const float lrtot = lrnd + partner(lrnd);
+  const float ltot = pair_sum(lsum);
   if (row_ok) {
-    const float inv = lrtot > 0.f ? 1.f / lrtot : 0.f;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(o[db][4 * rq + e] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * rq + 4 * g) = w;
+        const u32x2 w = {pack_bf16(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv),
+                         pack_bf16(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv)};
+        *(u32x2*)(orow + db * 32 + 8 * rq + 4 * g) = w;
       }
     }
     if (a.stats && g == 0) {
       float* st = a.stats + (((int64_t)b * a.Hq + h) * Lq + myq) * 2;
-      st[0] = m2 == -INFINITY ? -INFINITY : m2 * (1.f / kLog2e);
-      st[1] = ltot;
+      const bool any_key = m_true != -INFINITY;
+      st[0] = any_key ? m_true * (1.f / kLog2e) : -INFINITY;
+      // denominator relative to the true max
+      st[1] = any_key ? ltot * __builtin_amdgcn_exp2f(m_use - m_true) : 0.f;
     }
   }
 }
