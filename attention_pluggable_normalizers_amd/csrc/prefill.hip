@@ -105,67 +105,55 @@ __device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
   qb = nqb - 1 - (id - bh * nqb);
 }
 
+// Buffer resource over `bytes` bytes at `base`: raw buffer loads past the end
+// return zeros, which is how the ragged last key tile is read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// Global -> register -> LDS staging of one K tile (row-major, chunk-swizzled)
+// and one V tile (transposed).  Every thread loads KPT 16-byte K chunks and
+// VPT units of KPU keys x 8 dims of V.  Row strides are in bytes.
 template <class C>
 struct Tiles {
-  // global -> registers
+  static constexpr int KPU = ((C::BN / 4) * C::CPR >= C::NT) ? 4 : 2;
+  static constexpr int VUN = (C::BN / KPU) * C::CPR;
+  static constexpr int VPT = VUN / C::NT;
+  static_assert(VUN % C::NT == 0, "V tile must split evenly over the threads");
+  static constexpr int KROWS = C::NT / C::CPR;  // K rows covered by one pass of the threads
+  static constexpr int VROWS = KROWS * KPU;     // V rows covered by one pass of the threads
+
   u32x4 kr[C::KPT];
-  u32x4 vr[C::VPT][4];
+  u32x4 vr[VPT][KPU];
+  uint32_t kvoff, vvoff;  // per-thread byte offsets inside a tile
+  uint32_t kstr, vstr;    // row strides in bytes
 
-  __device__ __forceinline__ void load_k(const bf16_t* kb, int64_t ksl, int k0, int Lk, int tid) {
-    if (k0 + C::BN <= Lk) {  // whole tile in range (every tile but a ragged last one)
+  __device__ __forceinline__ void init(int64_t ksl, int64_t vsl, int tid) {
+    kstr = (uint32_t)(ksl * 2);
+    vstr = (uint32_t)(vsl * 2);
+    const int r = tid / C::CPR, ch = tid % C::CPR;
+    kvoff = r * kstr + ch * 16;
+    vvoff = r * KPU * vstr + ch * 16;
+  }
+  __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int k0) {
 #pragma unroll
-      for (int i = 0; i < C::KPT; ++i) {
-        const int id = tid + i * C::NT;
-        const int row = id / C::CPR, ch = id % C::CPR;
-        kr[i] = *(const u32x4*)(kb + (int64_t)(k0 + row) * ksl + ch * 8);
-      }
-      return;
-    }
+    for (int i = 0; i < C::KPT; ++i) kr[i] = buf_load16(rk, kvoff, (k0 + i * KROWS) * kstr);
+  }
+  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, int k0) {
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::CPR, ch = id % C::CPR;
-      const int key = k0 + row;
-      kr[i] = key < Lk ? *(const u32x4*)(kb + (int64_t)key * ksl + ch * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+      for (int j = 0; j < KPU; ++j) vr[i][j] = buf_load16(rv, vvoff, (k0 + i * VROWS + j) * vstr);
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k0) {
+    load_k(rk, k0);
+    load_v(rv, k0);
   }
 
-  __device__ __forceinline__ void load_v(const bf16_t* vb, int64_t vsl, int k0, int Lk, int tid) {
-    if (k0 + C::BN <= Lk) {
-#pragma unroll
-      for (int i = 0; i < C::VPT; ++i) {
-        const int id = tid + i * C::NT;
-        if (C::VUN % C::NT == 0 || id < C::VUN) {
-          const int kg = id / C::CPR, ch = id % C::CPR;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            vr[i][j] = *(const u32x4*)(vb + (int64_t)(k0 + kg * 4 + j) * vsl + ch * 8);
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i) {
-      const int id = tid + i * C::NT;
-      if (C::VUN % C::NT == 0 || id < C::VUN) {
-        const int kg = id / C::CPR, ch = id % C::CPR;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k0 + kg * 4 + j;
-          vr[i][j] = key < Lk ? *(const u32x4*)(vb + (int64_t)key * vsl + ch * 8)
-                              : u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void load(const bf16_t* kb, const bf16_t* vb, int64_t ksl,
-                                       int64_t vsl, int k0, int Lk, int tid) {
-    load_k(kb, ksl, k0, Lk, tid);
-    load_v(vb, vsl, k0, Lk, tid);
-  }
-
-  // registers -> LDS, K row-major
   __device__ __forceinline__ void store_k(bf16_t* kl, int tid) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
@@ -175,21 +163,21 @@ struct Tiles {
     }
   }
 
-  // registers -> LDS, V transposed
   __device__ __forceinline__ void store_v(bf16_t* vl, int tid) {
 #pragma unroll
-    for (int i = 0; i < C::VPT; ++i) {
+    for (int i = 0; i < VPT; ++i) {
       const int id = tid + i * C::NT;
-      if (C::VUN % C::NT == 0 || id < C::VUN) {
-        const int kg = id / C::CPR, ch = id % C::CPR;
-        const int pos = vt_pos(kg * 4);
-        const int pch = pos >> 3, poff = pos & 7;
+      const int kg = id / C::CPR, ch = id % C::CPR;
+      const int pos = vt_pos(kg * KPU);
+      const int pch = pos >> 3, poff = pos & 7;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {  // dword w of each key row = dims 2w, 2w+1
-          const unsigned a0 = vr[i][0][w], a1 = vr[i][1][w], a2 = vr[i][2][w], a3 = vr[i][3][w];
+      for (int w = 0; w < 4; ++w) {  // dword w of each key row = dims 2w, 2w+1
 #pragma unroll
-          for (int hbit = 0; hbit < 2; ++hbit) {
-            const int d = ch * 8 + 2 * w + hbit;
+        for (int hbit = 0; hbit < 2; ++hbit) {
+          const int d = ch * 8 + 2 * w + hbit;
+          bf16_t* dst = vl + d * C::BN + v_chunk<C::VSW>(d, pch) * 8 + poff;
+          if constexpr (KPU == 4) {
+            const unsigned a0 = vr[i][0][w], a1 = vr[i][1][w], a2 = vr[i][2][w], a3 = vr[i][3][w];
             u32x2 val;
             if (hbit == 0) {
               val[0] = (a0 & 0xffffu) | (a1 << 16);
@@ -198,7 +186,11 @@ struct Tiles {
               val[0] = (a0 >> 16) | (a1 & 0xffff0000u);
               val[1] = (a2 >> 16) | (a3 & 0xffff0000u);
             }
-            *(u32x2*)(vl + d * C::BN + v_chunk<C::VSW>(d, pch) * 8 + poff) = val;
+            *(u32x2*)dst = val;
+          } else {
+            const unsigned a0 = vr[i][0][w], a1 = vr[i][1][w];
+            *(unsigned*)dst = hbit == 0 ? ((a0 & 0xffffu) | (a1 << 16))
+                                        : ((a0 >> 16) | (a1 & 0xffff0000u));
           }
         }
       }
@@ -378,9 +370,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
   const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;
 
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
   Tiles<C> tiles;
+  tiles.init(a.k_sl, a.v_sl, tid);
   if (t0 < t1) {
-    tiles.load(kbase, vbase, a.k_sl, a.v_sl, t0 * C::BN, Lk, tid);
+    tiles.load(rk, rv, t0 * C::BN);
     tiles.store(kl0, vl0, tid);
   }
   __syncthreads();
@@ -389,7 +384,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
     const int cur = (t - t0) & 1;
     const bf16_t* kl = kl0 + cur * C::BN * C::D;
     const bf16_t* vl = vl0 + cur * C::BN * C::D;
-    if (t + 1 < t1) tiles.load(kbase, vbase, a.k_sl, a.v_sl, (t + 1) * C::BN, Lk, tid);
+    if (t + 1 < t1) tiles.load(rk, rv, (t + 1) * C::BN);
     const int k0 = t * C::BN;
     const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
@@ -691,16 +686,19 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     if (cnt + 16 > SCAP || pc + 16 > SCAP) ovf = true;
   };
 
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
   Tiles<C> tiles;
+  tiles.init(a.k_sl, a.v_sl, tid);
   if (t0 < t1) {
-    tiles.load_k(kbase, a.k_sl, t0 * C::BN, Lk, tid);
+    tiles.load_k(rk, t0 * C::BN);
     tiles.store_k(kl0, tid);
   }
   __syncthreads();
   for (int t = t0; t < t1; ++t) {
     const int cur = (t - t0) & 1;
     const bf16_t* kl = kl0 + cur * C::BN * C::D;
-    if (t + 1 < t1) tiles.load_k(kbase, a.k_sl, (t + 1) * C::BN, Lk, tid);
+    if (t + 1 < t1) tiles.load_k(rk, (t + 1) * C::BN);
     const int k0 = t * C::BN;
     const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
@@ -788,14 +786,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     float mn = INFINITY;
     const double mref = (double)mrun;
     if (t0 < t1) {
-      tiles.load_k(kbase, a.k_sl, t0 * C::BN, Lk, tid);
+      tiles.load_k(rk, t0 * C::BN);
       tiles.store_k(kl0, tid);
     }
     __syncthreads();
     for (int t = t0; t < t1; ++t) {
       const int cur = (t - t0) & 1;
       const bf16_t* kl = kl0 + cur * C::BN * C::D;
-      if (t + 1 < t1) tiles.load_k(kbase, a.k_sl, (t + 1) * C::BN, Lk, tid);
+      if (t + 1 < t1) tiles.load_k(rk, (t + 1) * C::BN);
       const int k0 = t * C::BN;
       const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(pending);
       if (active) {
@@ -852,7 +850,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
   if (t0 < t1) {
-    tiles.load(kbase, vbase, a.k_sl, a.v_sl, t0 * C::BN, Lk, tid);
+    tiles.load(rk, rv, t0 * C::BN);
     tiles.store(kl0, vl0, tid);
   }
   __syncthreads();
@@ -860,7 +858,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     const int cur = (t - t0) & 1;
     const bf16_t* kl = kl0 + cur * C::BN * C::D;
     const bf16_t* vl = vl0 + cur * C::BN * C::D;
-    if (t + 1 < t1) tiles.load(kbase, vbase, a.k_sl, a.v_sl, (t + 1) * C::BN, Lk, tid);
+    if (t + 1 < t1) tiles.load(rk, rv, (t + 1) * C::BN);
     const int k0 = t * C::BN;
     const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
@@ -957,6 +955,9 @@ bool prefill_mfma_supported(const FwdArgs& a) {
                        a.v_sb, a.v_sh, a.v_sl, a.o_sb, a.o_sh, a.o_sl};
   for (int64_t x : s)
     if (x % 8) return false;
+  // K/V slices are addressed through 32-bit buffer records
+  if ((int64_t)a.Lk * a.k_sl * 2 >= ((int64_t)1 << 31) || (int64_t)a.Lk * a.v_sl * 2 >= ((int64_t)1 << 31))
+    return false;
   const int nqb_min = (a.Lq + 127) / 128;
   return (int64_t)nqb_min * a.B * a.Hq <= (int64_t)INT32_MAX;
 }
