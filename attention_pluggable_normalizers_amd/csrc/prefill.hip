@@ -517,10 +517,11 @@ struct SparseCfg {
   static constexpr int REGION_BYTES = 65536 - 2 * C::BN * C::D * 2;  // V tiles / candidates
   static constexpr int SCAP = REGION_BYTES / (C::NT * 4);            // candidates per lane
   static_assert(REGION_BYTES >= 2 * C::BN * C::D * 2, "region must hold two V tiles");
-  static_assert(SCAP >= 17, "candidate buffer too small");
+  static_assert(SCAP >= 32 && SCAP % 8 == 0, "candidate buffer too small");
 };
 
 // z of one raw score q.k (the value the threshold acts on).
+// Monotone in raw (cz, capz > 0); a masked score (-inf) stays -inf.
 template <bool CAP>
 __device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, float capz) {
 #pragma clang fp contract(off)
@@ -528,9 +529,41 @@ __device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, fl
     const float y = raw * sc_over_cap;
     const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
     const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
-    return capz * t;
+    return raw == -INFINITY ? -INFINITY : capz * t;
   }
   return raw * cz;
+}
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = v[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, v[r]);
+  return m;
+}
+
+// Max of z over one 32-key block.  Without softcap z = cz * raw is monotone
+// under rounding, so z(max raw) is exact; the softcapped transform is taken
+// per element.
+template <bool CAP>
+__device__ __forceinline__ float block_zmax(const f32x16& v, float cz, float sc_over_cap, float capz) {
+  if (!CAP) return zval<false>(max16(v), cz, sc_over_cap, capz);
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, zval<true>(v[r], cz, sc_over_cap, capz));
+  return m;
+}
+
+// Sets scores of keys outside this lane's row interval to -inf.  `base` is
+// k0 + 4 * (lane / 32) - lo and `span` = hi - lo of the row.
+template <class C>
+__device__ __forceinline__ void mask_tile(f32x16* s, int base, int span) {
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+      s[kb][r] = off < (unsigned)span ? s[kb][r] : -INFINITY;
+    }
 }
 
 __device__ __forceinline__ double partner_d(double x) { return __shfl_xor(x, 32, 64); }
@@ -582,23 +615,31 @@ __device__ __forceinline__ float float_floor(double x) {
 }
 
 // Keeps this lane's candidates above t (compacting them) and returns their
-// partial sums of y = z - mref.
+// partial sums of y = z - mref.  Entries are read 8 at a time so their LDS
+// latencies overlap (SCAP is a multiple of 8, so the reads stay inside the
+// lane's buffer); compaction only writes to slots already read.
 template <int SCAP>
 __device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double mref, double& c,
                                          double& s1, double& s2, float& mn) {
+  static_assert(SCAP % 8 == 0, "buffer length must be a multiple of 8");
   int w = 0;
   c = s1 = s2 = 0.0;
   mn = INFINITY;
-  for (int e = 0; e < cnt; ++e) {
-    const float z = buf[e * 64];
-    if ((double)z > t) {
-      buf[w * 64] = z;
-      ++w;
-      const double y = (double)z - mref;
-      c += 1.0;
-      s1 += y;
-      s2 += y * y;
-      mn = fminf(mn, z);
+  for (int e0 = 0; e0 < cnt; e0 += 8) {
+    float z[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = buf[(e0 + j) * 64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (e0 + j < cnt && (double)z[j] > t) {
+        buf[w * 64] = z[j];
+        ++w;
+        const double y = (double)z[j] - mref;
+        c += 1.0;
+        s1 += y;
+        s2 += y * y;
+        mn = fminf(mn, z[j]);
+      }
     }
   }
   cnt = w;
@@ -704,22 +745,18 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     if (active) {
       f32x16 s[C::NKB];
       qk_tile<C>(kl, qreg, l32, g, s);
-      const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+      if ((k0 + C::BN > wfirst.hi) || (k0 < wlast.lo))
+        mask_tile<C>(s, k0 + 4 * g - mine.lo, mine.hi - mine.lo);
+      // z is monotone in the raw score: per-block maxima decide whether a
+      // block can hold a candidate at all
+      float bz[C::NKB];
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
-          if (edge) {
-            const int key = s_key(k0, kb, r, g);
-            if (key < mine.lo || key >= mine.hi) z = -INFINITY;
-          }
-          s[kb][r] = z;
-          mt = fmaxf(mt, z);
-        }
+        bz[kb] = block_zmax<CAP>(s[kb], cz, sc_over_cap, capz);
+        mt = fmaxf(mt, bz[kb]);
       }
-      mt = fmaxf(mt, partner(mt));
+      mt = pair_max(mt);
       if (mt > mrun) {
         mrun = mt;
         const double fl = (double)mrun - 1.0;
@@ -730,17 +767,20 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       }
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        bool any = false;
+        if (__any(bz[kb] > floor_f && !ovf)) {
+          float z[16];
+          int na = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) any |= s[kb][r] > floor_f;
-        if (__any(any && !ovf)) {
+          for (int r = 0; r < 16; ++r) {
+            z[r] = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
+            na += z[r] > floor_f ? 1 : 0;
+          }
           if (__any(!ovf && cnt + 16 > SCAP)) refloor();
-          if (!ovf) {
+          if (!ovf && na > 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float z = s[kb][r];
-              if (z > floor_f) {
-                buf[cnt * 64] = z;
+              if (z[r] > floor_f) {
+                buf[cnt * 64] = z[r];
                 ++cnt;
               }
             }
