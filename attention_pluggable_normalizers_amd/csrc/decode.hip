@@ -1,8 +1,595 @@
-// Paged split-KV decode kernels.  Placeholder until implemented.
+// Paged decode (one query token per sequence) with split-KV reduction.
+//
+// The K/V cache is read page by page through the block table ("HF Attention
+// Normalizers", "Differentiable Paged Attention": physical pages are read
+// directly, no gathered K/V copy).  The keys of a sequence are cut into
+// splits of kSplit keys; one wave handles one (split, kv head, sequence) and
+// serves all G = Hq / Hkv query heads of the group, so every K/V byte is read
+// once:
+//
+//   scores  S^T (16 keys x 16 query heads) = K_block . Q^T on
+//           v_mfma_f32_16x16x32_bf16; lanes 0..G-1 of each 16 hold real
+//           heads, K rows are loaded straight from their pages;
+//   softmax / softmax1: online (max, sum) per head over the split, then the
+//           weighted sum of V on the vector ALUs (each lane owns 8 dims of
+//           one key row per step), written as a partial (m, l, acc[D]);
+//           a combine kernel merges the partials ("two-stage KV-tile
+//           reduction without atomics", same page) and adds softmax1's "+1";
+//   sparsemax / entmax15: the split kernel stores z for every key; a solver
+//           kernel per (sequence, query head) finds the row threshold over
+//           the candidates above (max z - 1) kept in LDS, then sums
+//           g(z - tau) V over the support only, so V rows of zero-weight keys
+//           are never read.
+
 #include "common.h"
 
 namespace attn {
-bool decode_supported(const FwdArgs&) { return false; }
-size_t decode_workspace_bytes(const FwdArgs&) { return 0; }
-hipError_t launch_decode(const FwdArgs&, void*, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSplit = 512;      // keys per split
+constexpr int kSolveCap = 4096;  // candidate capacity of the sparse solver (LDS)
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+struct SeqView {
+  int n;    // live keys of the sequence (clamped to the table's reach)
+  int lo;   // first visible key (sliding window)
+};
+
+__device__ __forceinline__ SeqView seq_view(const FwdArgs& a, int b) {
+  SeqView v;
+  v.n = max(0, min(a.seq_lens[b], a.max_blocks * a.block_size));
+  // one query at position n - 1 (bottom-right): causal keeps every live key
+  v.lo = a.window ? max(0, v.n - a.window) : 0;
+  return v;
+}
+
+// Byte offset of key j's row (kv head folded into `head_off`) in a cache.
+__device__ __forceinline__ int64_t key_row(const int32_t* table, int bs, int64_t sb, int64_t sl, int j) {
+  const int64_t page = table[j / bs];
+  return page * sb + (int64_t)(j % bs) * sl;
+}
+
+// Partial record per (sequence, query head, split): m, l, acc[D] (fp32).
+__device__ __forceinline__ float* partial_ptr(float* ws, const FwdArgs& a, int b, int qh, int s, int ns) {
+  return ws + (((int64_t)b * a.Hq + qh) * ns + s) * (a.D + 2);
+}
+
+// GM: compile-time bound on the group size G (query heads per kv head).
+template <int D, int NORM, bool CAP, int GM>
+__global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, int ns) {
+  constexpr int NKC = D / 32;     // k-steps of the 16x16x32 QK product
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int KS = 64 / CPR;    // key rows per PV step (lanes per chunk column)
+  __shared__ float ps[32][17];    // weights of the 32 keys of a chunk, per head (padded)
+
+  const int lane = threadIdx.x;
+  const int s = blockIdx.x % ns;
+  const int bh = blockIdx.x / ns;
+  const int kvh = bh % a.Hkv;
+  const int b = bh / a.Hkv;
+  const int G = a.G;
+  const SeqView sv = seq_view(a, b);
+  const int k_begin = max(sv.lo, s * kSplit);
+  const int k_end = min(sv.n, (s + 1) * kSplit);
+
+  const int hh = lane & 15;        // query head of this lane's MFMA column
+  const bool head_ok = hh < G;
+  const int qh = kvh * G + (head_ok ? hh : 0);
+  const int32_t* table = a.block_table + (int64_t)b * a.max_blocks;
+  const bf16_t* kc = (const bf16_t*)a.k + (int64_t)kvh * a.k_sh;
+  const bf16_t* vc = (const bf16_t*)a.v + (int64_t)kvh * a.v_sh;
+
+  if (k_begin >= k_end) {
+    // empty split: neutral partial (m = -inf, l = 0, acc = 0)
+    if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1) {
+      for (int h = 0; h < G; ++h) {
+        float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
+        for (int d = lane; d < D + 2; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
+      }
+    }
+    return;
+  }
+
+  // Q^T operand: lane l holds head l%16, dims 32c + 8 (l/16) .. +7
+  bf16x8 qreg[NKC];
+  {
+    const bf16_t* qrow = (const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)qh * a.q_sh;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+      qreg[c] = head_ok ? *(const bf16x8*)(qrow + 32 * c + 8 * (lane >> 4)) : bf16x8{};
+  }
+  const float scale = NORM == ATTN_ENTMAX15 ? 0.5f * a.scaling : a.scaling;  // z units
+  const float c2 = a.scaling * kLog2e;
+  const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
+  const float capz = CAP ? (NORM == ATTN_ENTMAX15 ? 0.5f : 1.f) * a.softcap : 0.f;
+
+  // PV lane layout: key slot ks = lane / CPR, 8 dims from chunk ch = lane % CPR
+  const int ks = lane / CPR, ch = lane % CPR;
+  float acc[GM][8];  // [head][dim] for this lane's chunk (heads < G used)
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  float m2 = -INFINITY;  // running max of this lane's head, log2 units
+  float lsum = 0.f;      // running sum (this lane's keys only; reduced at the end)
+
+  float* zrow = (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15)
+                    ? ws + ((int64_t)b * a.Hq + qh) * ((int64_t)a.max_blocks * a.block_size)
+                    : nullptr;
+
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    // ---- scores of keys k0 .. k0+31 (two 16-key MFMA blocks)
+    f32x4 sacc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int j = k0 + sb * 16 + (lane & 15);
+      const int jj = min(j, k_end - 1);  // rows past the end are masked below
+      const bf16_t* krow = kc + key_row(table, a.block_size, a.k_sb, a.k_sl, jj);
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const bf16x8 kv = *(const bf16x8*)(krow + 32 * c + 8 * (lane >> 4));
+        sacc[sb] = mfma16(kv, qreg[c], sacc[sb]);
+      }
+    }
+    // lane holds head hh, keys k0 + 16 sb + 4 (lane/16) + r
+    float x[8];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = k0 + sb * 16 + 4 * (lane >> 4) + r;
+        float v = sacc[sb][r];
+        if (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
+          if (CAP) {
+            const float y = v * sc_over_cap;
+            const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
+            v = capz * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
+          } else {
+            v = v * scale;
+          }
+        } else {
+          if (CAP) {
+            const float y = v * sc_over_cap;
+            const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
+            v = a.softcap * kLog2e * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
+          } else {
+            v = v * c2;
+          }
+        }
+        x[sb * 4 + r] = j < k_end ? v : -INFINITY;
+      }
+
+    if (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
+      // store z for the solver (16 bytes per lane and block)
+      if (head_ok) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int j = k0 + sb * 16 + 4 * (lane >> 4);
+          if (j + 3 < k_end) {
+            *(f32x4*)(zrow + j) = f32x4{x[sb * 4], x[sb * 4 + 1], x[sb * 4 + 2], x[sb * 4 + 3]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (j + r < k_end) zrow[j + r] = x[sb * 4 + r];
+          }
+        }
+      }
+      continue;
+    }
+
+    // ---- online softmax per head (lanes sharing lane%16 share the head)
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mt = fmaxf(mt, x[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m2, mt);
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);
+    m2 = m_new;
+    lsum *= alpha;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+      lsum += p[i];
+    }
+    // weights to LDS: ps[key][head]
+    __syncthreads();  // previous chunk's PV reads are done
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ps[sb * 16 + 4 * (lane >> 4) + r][hh] = p[sb * 4 + r];
+    // alpha of every head, for the PV accumulators
+    __shared__ float alph[16];
+    if (lane < 16) alph[lane] = alpha;
+    __syncthreads();
+    float al[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) al[h] = alph[h];
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+      if (h < G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+    // ---- weighted sum of V: rows k0 + ks, k0 + ks + KS, ...
+    for (int kk = ks; kk < 32; kk += KS) {
+      const int j = k0 + kk;
+      if (j < k_end) {
+        const bf16_t* vrow = vc + key_row(table, a.block_size, a.v_sb, a.v_sl, j);
+        const u32x4 w = *(const u32x4*)(vrow + 8 * ch);
+        float vv[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vv[2 * q] = bf_lo(w[q]);
+          vv[2 * q + 1] = bf_hi(w[q]);
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+          if (h < G) {
+            const float pj = ps[kk][h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pj, vv[e], acc[h][e]);
+          }
+      }
+    }
+  }
+
+  if (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) return;
+
+  // ---- partial record: reduce acc over the KS key slots, l over the 4 lanes of a head
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[h][e];
+        for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        acc[h][e] = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h >= G) break;
+    float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
+    if (lane == h) {
+      pp[0] = m2;
+      pp[1] = lsum;
+    }
+    if (ks == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pp[2 + 8 * ch + e] = acc[h][e];
+    }
+  }
+}
+
+// Merge the split partials of one (sequence, query head).  All in log2 units.
+template <int D, int NORM>
+__global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const float* ws, int ns) {
+  const int row = blockIdx.x;  // b * Hq + qh
+  const int b = row / a.Hq, qh = row - b * a.Hq;
+  const int tid = threadIdx.x;
+  __shared__ float red[256];
+  // global max over the splits (softmax1 also counts its logit-0 sink)
+  float m = -INFINITY;
+  for (int s = tid; s < ns; s += 256) m = fmaxf(m, ws[((int64_t)row * ns + s) * (D + 2)]);
+  red[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  float M = red[0];
+  __syncthreads();
+  if (NORM == ATTN_SOFTMAX1) M = fmaxf(M, 0.f);
+  const float mref = M == -INFINITY ? 0.f : M;
+  float l = 0.f;
+  for (int s = tid; s < ns; s += 256) {
+    const float* pp = ws + ((int64_t)row * ns + s) * (D + 2);
+    l += pp[1] * __builtin_amdgcn_exp2f(pp[0] - mref);
+  }
+  red[tid] = l;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  float L = red[0];
+  if (NORM == ATTN_SOFTMAX1) L += __builtin_amdgcn_exp2f(-mref);  // the "+1" at logit 0
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)qh * a.o_sh;
+  for (int d = tid; d < D; d += 256) {
+    float acc = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float* pp = ws + ((int64_t)row * ns + s) * (D + 2);
+      const float w = __builtin_amdgcn_exp2f(pp[0] - mref);
+      acc = fmaf(w, pp[2 + d], acc);
+    }
+    orow[d] = (bf16_t)(acc * inv);
+  }
+  if (a.stats && tid == 0) {
+    float* st = a.stats + (int64_t)row * 2;
+    const bool any = M != -INFINITY;
+    st[0] = any ? M * (1.f / kLog2e) : -INFINITY;
+    st[1] = any ? L : 0.f;
+  }
+}
+
+// Block-wide reductions over 256 threads.
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_min(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fminf(fminf(red[0], red[1]), fminf(red[2], red[3]));
+}
+
+// Threshold search step over the candidate set L = {z > t} (see the
+// prefill kernels): returns tau when the closed form over L lies below every
+// member of L (then L is the support), else a larger lower bound.
+template <int NORM>
+__device__ __forceinline__ double solve_step(double c, double s1, double s2, float mn, double mref,
+                                             double t, bool& exact) {
+  const double ty = t - mref;
+  double tcf, step;
+  bool valid;
+  if (NORM == ATTN_SPARSEMAX) {
+    tcf = (s1 - 1.0) / c;
+    valid = true;
+    step = tcf;
+  } else {
+    const double mu = s1 / c;
+    const double ss = s2 - s1 * mu;
+    const double delta = (1.0 - ss) / c;
+    valid = delta >= 0.0;
+    tcf = valid ? mu - sqrt(delta) : 0.0;
+    const double f = s2 - 2.0 * ty * s1 + c * ty * ty - 1.0;
+    const double fp = 2.0 * (s1 - c * ty);
+    step = ty + f / fp;
+  }
+  const double mny = (double)mn - mref;
+  if (valid && tcf < mny) {
+    exact = true;
+    return mref + tcf;
+  }
+  exact = false;
+  return mref + fmax(step, mny);
+}
+
+// One (sequence, query head) row of a sparse normalizer: threshold, then the
+// weighted sum of the support's V rows.
+template <int D, int NORM>
+__global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, const float* ws) {
+  __shared__ float cz[kSolveCap];
+  __shared__ int ci[kSolveCap];
+  __shared__ double redd[4];
+  __shared__ float redf[4];
+  __shared__ float oacc[4][D];
+
+  const int row = blockIdx.x;
+  const int b = row / a.Hq, qh = row - b * a.Hq, kvh = qh / a.G;
+  const int tid = threadIdx.x;
+  const SeqView sv = seq_view(a, b);
+  const float* z = ws + (int64_t)row * ((int64_t)a.max_blocks * a.block_size);
+  bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)qh * a.o_sh;
+
+  if (sv.lo >= sv.n) {  // no visible key
+    for (int d = tid; d < D; d += 256) orow[d] = (bf16_t)0.f;
+    if (a.stats && tid == 0) {
+      a.stats[(int64_t)row * 2] = INFINITY;
+      a.stats[(int64_t)row * 2 + 1] = 0.f;
+    }
+    return;
+  }
+  // row max
+  float m = -INFINITY;
+  for (int j = sv.lo + tid; j < sv.n; j += 256) m = fmaxf(m, z[j]);
+  m = block_max(m, redf);
+  const double mref = (double)m;
+  // candidates above m - 1 (tau >= m - 1) into LDS, in key order (ballot
+  // prefix sums), so every later sum runs in a fixed order
+  __shared__ int wcnt[4];
+  double t = mref - 1.0;
+  int base = 0;
+  const int wv = tid >> 6, ln0 = tid & 63;
+  for (int j0 = sv.lo; j0 < sv.n; j0 += 256) {
+    const int j = j0 + tid;
+    const float v = j < sv.n ? z[j] : -INFINITY;
+    const bool flag = (double)v > t;
+    const unsigned long long bal = __ballot(flag);
+    const int before = __popcll(bal & ((1ull << ln0) - 1ull));
+    if (ln0 == 0) wcnt[wv] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w2 = 0; w2 < wv; ++w2) off += wcnt[w2];
+    const int slot = off + before;
+    if (flag && slot < kSolveCap) {
+      cz[slot] = v;
+      ci[slot] = j;
+    }
+    base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
+  }
+  const int ncand = base;
+  const bool in_lds = ncand <= kSolveCap;
+  // Newton / closed form over {z > t}, on the LDS candidates or the row itself
+  double tau = INFINITY;
+  double ksup = 0.0;
+  const int lim = (in_lds ? ncand : sv.n - sv.lo) + 2;
+  for (int it = 0; it < lim; ++it) {
+    double c = 0.0, s1 = 0.0, s2 = 0.0;
+    float mn = INFINITY;
+    if (in_lds) {
+      for (int e = tid; e < ncand; e += 256) {
+        const float v = cz[e];
+        if ((double)v > t) {
+          const double y = (double)v - mref;
+          c += 1.0;
+          s1 += y;
+          s2 += y * y;
+          mn = fminf(mn, v);
+        }
+      }
+    } else {
+      for (int j = sv.lo + tid; j < sv.n; j += 256) {
+        const float v = z[j];
+        if ((double)v > t) {
+          const double y = (double)v - mref;
+          c += 1.0;
+          s1 += y;
+          s2 += y * y;
+          mn = fminf(mn, v);
+        }
+      }
+    }
+    c = block_sum(c, redd);
+    s1 = block_sum(s1, redd);
+    s2 = block_sum(s2, redd);
+    mn = block_min(mn, redf);
+    bool ex;
+    const double tn = solve_step<NORM>(c, s1, s2, mn, mref, t, ex);
+    if (ex) {
+      tau = tn;
+      ksup = c;
+      break;
+    }
+    t = fmax(t, tn);
+  }
+  // weighted sum of V over the support: 4 waves split the keys, lanes own dims
+  const float tauf = (float)tau;
+  const int w = tid >> 6, ln = tid & 63;
+  constexpr int DPL = D / 64;  // dims per lane
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  const int32_t* table = a.block_table + (int64_t)b * a.max_blocks;
+  const bf16_t* vc = (const bf16_t*)a.v + (int64_t)kvh * a.v_sh;
+  auto add_key = [&](int j, float v) {
+    const float d = v - tauf;
+    if (d > 0.f) {
+      const float p = NORM == ATTN_ENTMAX15 ? d * d : d;
+      const bf16_t* vrow = vc + key_row(table, a.block_size, a.v_sb, a.v_sl, j);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, (float)vrow[ln * DPL + e], acc[e]);
+    }
+  };
+  if (in_lds) {
+    for (int e = w; e < ncand; e += 4) add_key(ci[e], cz[e]);  // wave-uniform key
+  } else {
+    for (int j = sv.lo + w; j < sv.n; j += 4) add_key(j, z[j]);
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) oacc[w][ln * DPL + e] = acc[e];
+  __syncthreads();
+  for (int d = tid; d < D; d += 256)
+    orow[d] = (bf16_t)(oacc[0][d] + oacc[1][d] + oacc[2][d] + oacc[3][d]);
+  if (a.stats && tid == 0) {
+    a.stats[(int64_t)row * 2] = (float)tau;
+    a.stats[(int64_t)row * 2 + 1] = (float)ksup;
+  }
+}
+
+int num_splits(const FwdArgs& a) {
+  const int64_t maxlen = (int64_t)a.max_blocks * a.block_size;
+  return (int)((maxlen + kSplit - 1) / kSplit);
+}
+
+template <int D, int NORM>
+hipError_t launch_d(const FwdArgs& a, void* workspace, hipStream_t stream) {
+  float* ws = (float*)workspace;
+  const int ns = num_splits(a);
+  const bool cap = a.softcap > 0.f;
+  dim3 g1((unsigned)((int64_t)a.B * a.Hkv * ns)), b1(64);
+  if (a.G <= 4) {
+    if (cap) decode_split_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
+    else decode_split_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
+  } else if (a.G <= 8) {
+    if (cap) decode_split_kernel<D, NORM, true, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
+    else decode_split_kernel<D, NORM, false, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
+  } else {
+    if (cap) decode_split_kernel<D, NORM, true, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+    else decode_split_kernel<D, NORM, false, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2((unsigned)((int64_t)a.B * a.Hq)), b2(256);
+  if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1)
+    decode_combine_kernel<D, NORM><<<g2, b2, 0, stream>>>(a, ws, ns);
+  else
+    decode_sparse_solve_kernel<D, NORM><<<g2, b2, 0, stream>>>(a, ws);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dn(const FwdArgs& a, void* workspace, hipStream_t stream) {
+  switch (a.norm) {
+    case ATTN_SOFTMAX: return launch_d<D, ATTN_SOFTMAX>(a, workspace, stream);
+    case ATTN_SOFTMAX1: return launch_d<D, ATTN_SOFTMAX1>(a, workspace, stream);
+    case ATTN_SPARSEMAX: return launch_d<D, ATTN_SPARSEMAX>(a, workspace, stream);
+    default: return launch_d<D, ATTN_ENTMAX15>(a, workspace, stream);
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+bool decode_supported(const FwdArgs& a) {
+  if (a.dtype != ATTN_BF16 || !a.paged || a.Lq != 1) return false;
+  if (a.D != 64 && a.D != 128 && a.D != 256) return false;
+  if (a.G < 1 || a.G > 16) return false;
+  if (!(a.scaling > 0.f)) return false;
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v)) return false;
+  const int64_t s[] = {a.q_sb, a.q_sh, a.k_sb, a.k_sh, a.k_sl, a.v_sb, a.v_sh, a.v_sl};
+  for (int64_t x : s)
+    if (x % 8) return false;
+  return true;
+}
+
+size_t decode_workspace_bytes(const FwdArgs& a) {
+  if (a.norm == ATTN_SOFTMAX || a.norm == ATTN_SOFTMAX1)
+    return (size_t)a.B * a.Hq * num_splits(a) * (a.D + 2) * sizeof(float);
+  return (size_t)a.B * a.Hq * ((size_t)a.max_blocks * a.block_size) * sizeof(float);
+}
+
+hipError_t launch_decode(const FwdArgs& a, void* workspace, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_dn<64>(a, workspace, stream);
+    case 128: return launch_dn<128>(a, workspace, stream);
+    default: return launch_dn<256>(a, workspace, stream);
+  }
+}
+
 }  // namespace attn

@@ -141,13 +141,14 @@ def gather_paged_kv(cache, block_table, seq_len, b):
     Attention").  Returns [Hkv, seq_len, D]: the live tokens only, so the
     unused tail of the last page is never touched.
     """
-    cache = _as_f64(cache)
     table = np.asarray(block_table)
     bs = cache.shape[1]
     n = int(seq_len)
     pages = [int(table[b, j]) for j in range((n + bs - 1) // bs)]
-    tokens = np.concatenate([cache[p] for p in pages], axis=0)[:n] if pages else \
-        np.zeros((0,) + cache.shape[2:])
+    if not pages:
+        return np.zeros((cache.shape[2], 0, cache.shape[3]))
+    # upcast only this sequence's pages (the cache can be far larger)
+    tokens = np.concatenate([_as_f64(cache[p]) for p in pages], axis=0)[:n]
     return np.transpose(tokens, (1, 0, 2))
 
 
