@@ -39,14 +39,25 @@ def credited_pairs(cfg):
     return total * cfg.B * cfg.Hq
 
 
-def decode_bytes(x, cfg, seq_lens):
-    """Bytes the paged decode must move: live K and V rows, q, out, table, lengths."""
+def decode_bytes(x, cfg, seq_lens, norm, support=None):
+    """Bytes the paged decode must move for one normalizer.
+
+    softmax / softmax1: every live K and V row.  sparsemax / entmax15: every
+    live K row (all scores are needed for the threshold) but only the V rows
+    of the support; `support` is the per-(sequence, query head) support size
+    from row_stats, so V is counted once per query head (an upper bound on
+    the union over the heads of a group).  Plus q, out, the used block-table
+    entries and the sequence lengths.
+    """
     live = int(sum(seq_lens))
-    kv = live * cfg.Hkv * cfg.D * 2 * 2
+    k = live * cfg.Hkv * cfg.D * 2
+    if norm in ("softmax", "softmax1"):
+        v = k
+    else:
+        v = int(round(float(support.sum()))) * cfg.D * 2
     q = cfg.B * cfg.Hq * cfg.D * 2
-    out = q
     table = sum(x.extra["pages"]) * 4
-    return kv + q + out + table + cfg.B * 4
+    return k + v + q + q + table + cfg.B * 4
 
 
 def cpu_baseline(cfg, budget_s=15.0):
@@ -183,7 +194,6 @@ def main():
                  "block_size": x.block_size, "max_blocks": x.max_blocks}
         dout = torch.empty_like(x.q)
         dst = torch.empty(*x.q.shape[:3], 2, dtype=torch.float32, device=dev)
-        nbytes = decode_bytes(x, dcfg, lens)
         dres = {}
         for n in dcfg.normalizers:
             ws_n = apn.attn_fwd_workspace_bytes(x.q, x.k_cache, x.v_cache, normalizer=n,
@@ -204,9 +214,13 @@ def main():
                 ts.append((e0, e1))
             torch.cuda.synchronize()
             ms = sorted(a.elapsed_time(b) for a, b in ts)[len(ts) // 2]
-            dres[n] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            nbytes = decode_bytes(x, dcfg, lens, n, dst[..., 1].cpu())
+            dres[n] = {"us": round(ms * 1e3, 1), "bytes": nbytes,
+                       "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                        "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        result["decode"] = {"workload": dcfg.name, "bytes": nbytes, "per_normalizer": dres}
+        result["decode"] = {"workload": dcfg.name, "B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv,
+                            "head_dim": dcfg.D, "block_size": dcfg.block_size,
+                            "live_keys": int(sum(lens)), "per_normalizer": dres}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)
