@@ -98,6 +98,8 @@ int validate(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
     a->seq_lens = paged->seq_lens;
     a->block_size = paged->block_size;
     a->max_blocks = paged->max_blocks;
+    if (k->shape[0] > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "too many cache pages");
+    a->num_blocks = (int)k->shape[0];
   }
   if (Hkv <= 0 && Hq > 0) return fail(ATTN_E_INVALID, "k/v have no heads");
   if (Hkv > 0 && Hq % Hkv != 0) return fail(ATTN_E_INVALID, "Hq must be a multiple of Hkv");

@@ -29,11 +29,22 @@ struct FwdArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int block_size, max_blocks;
+  int num_blocks;  // pages in each paged cache (page indices are clamped to it)
   int norm, causal, window;
   float softcap, scaling;
 };
 
 typedef __bf16 bf16_t;
+
+// Paged caches: live keys of sequence b (clamped to the table's reach; none
+// when the cache has no pages) and a block-table entry clamped into the
+// cache, so a bad entry yields wrong values instead of a stray access.
+__device__ __forceinline__ int paged_live(const FwdArgs& a, int b) {
+  return a.num_blocks > 0 ? max(0, min(a.seq_lens[b], a.max_blocks * a.block_size)) : 0;
+}
+__device__ __forceinline__ int64_t page_of(const int32_t* table_row, int idx, int num_blocks) {
+  return (int64_t)min(max(table_row[idx], 0), num_blocks - 1);
+}
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }

@@ -48,15 +48,16 @@ struct SeqView {
 
 __device__ __forceinline__ SeqView seq_view(const FwdArgs& a, int b) {
   SeqView v;
-  v.n = max(0, min(a.seq_lens[b], a.max_blocks * a.block_size));
+  v.n = paged_live(a, b);
   // one query at position n - 1 (bottom-right): causal keeps every live key
   v.lo = a.window ? max(0, v.n - a.window) : 0;
   return v;
 }
 
 // Byte offset of key j's row (kv head folded into `head_off`) in a cache.
-__device__ __forceinline__ int64_t key_row(const int32_t* table, int bs, int64_t sb, int64_t sl, int j) {
-  const int64_t page = table[j / bs];
+__device__ __forceinline__ int64_t key_row(const int32_t* table, int bs, int nb, int64_t sb, int64_t sl,
+                                           int j) {
+  const int64_t page = page_of(table, j / bs, nb);
   return page * sb + (int64_t)(j % bs) * sl;
 }
 
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
       sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int j = k0 + sb * 16 + (lane & 15);
       const int jj = min(j, k_end - 1);  // rows past the end are masked below
-      const bf16_t* krow = kc + key_row(table, a.block_size, a.k_sb, a.k_sl, jj);
+      const bf16_t* krow = kc + key_row(table, a.block_size, a.num_blocks, a.k_sb, a.k_sl, jj);
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
         const bf16x8 kv = *(const bf16x8*)(krow + 32 * c + 8 * (lane >> 4));
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
     for (int kk = ks; kk < 32; kk += KS) {
       const int j = k0 + kk;
       if (j < k_end) {
-        const bf16_t* vrow = vc + key_row(table, a.block_size, a.v_sb, a.v_sl, j);
+        const bf16_t* vrow = vc + key_row(table, a.block_size, a.num_blocks, a.v_sb, a.v_sl, j);
         const u32x4 w = *(const u32x4*)(vrow + 8 * ch);
         float vv[8];
 #pragma unroll
@@ -261,6 +262,281 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
         for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
         acc[h][e] = v;
       }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h >= G) break;
+    float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
+    if (lane == h) {
+      pp[0] = m2;
+      pp[1] = lsum;
+    }
+    if (ks == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pp[2 + 8 * ch + e] = acc[h][e];
+    }
+  }
+}
+
+// Raw buffer access: a load at byte offset >= `bytes` returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// Split kernel for caches whose page size is a multiple of 16 keys, so a
+// 16-key block never straddles two pages.  The split is walked in 16-key
+// blocks aligned to the page grid; lane i holds the page and in-page row of
+// block i (a split of 512 keys spans at most 33 blocks), so no block-table
+// read sits on the load path.  Each block is read through a buffer resource
+// whose size is the block's live rows: rows past the sequence end read as
+// zeros, so neither K nor V of a partial last page is touched.  K of the next
+// 32-key chunk and V of the current one are in flight while the current
+// chunk's scores, weights and PV sum are computed.
+template <int D, int NORM, bool CAP, int GM>
+__global__ __launch_bounds__(64) void decode_split_paged16_kernel(FwdArgs a, float* ws, int ns) {
+  constexpr bool SPARSE = NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15;
+  constexpr int NKC = D / 32;     // k-steps of the 16x16x32 QK product
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int KS = 64 / CPR;    // key rows per PV step (lanes per chunk column)
+  constexpr int RPB = 16 / KS;    // V rows per lane per 16-key block
+  constexpr int NV = 32 / KS;     // V rows per lane per 32-key chunk
+  __shared__ float ps[32][GM];    // weights of the chunk's keys, per head
+
+  const int lane = threadIdx.x;
+  const int s = blockIdx.x % ns;
+  const int bh = blockIdx.x / ns;
+  const int kvh = bh % a.Hkv;
+  const int b = bh / a.Hkv;
+  const int G = a.G;
+  const SeqView sv = seq_view(a, b);
+  const int k_begin = max(sv.lo, s * kSplit);
+  const int k_end = min(sv.n, (s + 1) * kSplit);
+
+  const int hh = lane & 15;
+  const bool head_ok = hh < G;
+  const int qh = kvh * G + (head_ok ? hh : 0);
+
+  if (k_begin >= k_end) {
+    if (!SPARSE) {
+      for (int h = 0; h < G; ++h) {
+        float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
+        for (int d = lane; d < D + 2; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
+      }
+    }
+    return;
+  }
+
+  // blocks of the split: lane i < nblk holds block i's K and V row
+  // addresses and live byte ranges; other lanes hold empty ranges
+  const int kb = k_begin & ~15;
+  const int nblk = (k_end - kb + 15) >> 4;
+  const int nchunk = (nblk + 1) >> 1;
+  uint64_t kaddr = 0, vaddr = 0;
+  uint32_t kbytes = 0, vbytes = 0;
+  if (lane < nblk) {
+    const int j0 = kb + 16 * lane;
+    const int pi = j0 / a.block_size;
+    const int64_t pg = page_of(a.block_table + (int64_t)b * a.max_blocks, pi, a.num_blocks);
+    const int64_t r = j0 - (int64_t)pi * a.block_size;
+    const int live = min(16, k_end - j0);
+    kaddr = (uint64_t)((const bf16_t*)a.k + (int64_t)kvh * a.k_sh + pg * a.k_sb + r * a.k_sl);
+    vaddr = (uint64_t)((const bf16_t*)a.v + (int64_t)kvh * a.v_sh + pg * a.v_sb + r * a.v_sl);
+    kbytes = (uint32_t)(live * a.k_sl * 2);
+    vbytes = (uint32_t)(live * a.v_sl * 2);
+  }
+  // resource over block c's live rows; c may run up to nblk + 2 (< 64), where
+  // the range is empty and loads return zeros without touching memory
+  auto block_rsrc = [&](uint64_t addr, uint32_t bytes, int c) __attribute__((always_inline)) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)addr, c);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(addr >> 32), c);
+    const uint32_t n = __builtin_amdgcn_readlane(bytes, c);
+    return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), n);
+  };
+
+  // Q^T operand: lane l holds head l%16, dims 32c + 8 (l/16) .. +7
+  bf16x8 qreg[NKC];
+  {
+    const bf16_t* qrow = (const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)qh * a.q_sh;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+      qreg[c] = head_ok ? *(const bf16x8*)(qrow + 32 * c + 8 * (lane >> 4)) : bf16x8{};
+  }
+  const float scale = NORM == ATTN_ENTMAX15 ? 0.5f * a.scaling : a.scaling;  // z units
+  const float c2 = a.scaling * kLog2e;
+  const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
+  const float capz = CAP ? (NORM == ATTN_ENTMAX15 ? 0.5f : 1.f) * a.softcap : 0.f;
+
+  const uint32_t k_voff = (uint32_t)((lane & 15) * a.k_sl * 2 + 16 * (lane >> 4));
+  const int ks = lane / CPR, ch = lane % CPR;
+  const uint32_t v_voff = (uint32_t)(ks * a.v_sl * 2 + 16 * ch);
+  const uint32_t v_step = (uint32_t)(KS * a.v_sl * 2);
+
+  typedef bf16x8 KTile[2][NKC];   // K rows of one 32-key chunk (two 16-key blocks)
+  auto load_k = [&](KTile& kt, int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const __amdgpu_buffer_rsrc_t rk = block_rsrc(kaddr, kbytes, 2 * t + sb);
+#pragma unroll
+      for (int c = 0; c < NKC; ++c)
+        kt[sb][c] = __builtin_bit_cast(bf16x8, buf_load16(rk, k_voff + 64 * c, 0));
+    }
+  };
+  // scores of chunk t in z units (sparse) or log2 units (softmax family);
+  // lane holds head hh, keys k0 + 16 sb + 4 (lane/16) + r at x[4 sb + r]
+  auto scores = [&](const KTile& kt, int t, float (&x)[8]) __attribute__((always_inline)) {
+    const int k0 = kb + 32 * t;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) sacc = mfma16(kt[sb][c], qreg[c], sacc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = k0 + sb * 16 + 4 * (lane >> 4) + r;
+        float v = sacc[r];
+        if (CAP) {
+          const float y = v * sc_over_cap;
+          const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
+          const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
+          v = SPARSE ? capz * th : a.softcap * kLog2e * th;
+        } else {
+          v = v * (SPARSE ? scale : c2);
+        }
+        x[sb * 4 + r] = (j >= k_begin && j < k_end) ? v : -INFINITY;
+      }
+    }
+  };
+
+  if (SPARSE) {
+    // z rows of the group's heads behind one resource; padding heads (and
+    // the empty block past an odd block count) store out of range, which
+    // drops the store, so every store is issued unconditionally.  Keys of a
+    // real block outside [k_begin, k_end) store -inf at positions no solver
+    // reads (below the window, or up to the next multiple of 16 past the
+    // sequence end, inside the row since pages hold 16k keys).
+    const int64_t zlen = (int64_t)a.max_blocks * a.block_size;
+    const int zrow0 = __builtin_amdgcn_readfirstlane(b * a.Hq + kvh * G);  // uniform
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(ws + (int64_t)zrow0 * zlen, (uint32_t)(G * zlen * 4));
+    const uint32_t zoff = head_ok ? (uint32_t)(hh * zlen * 4 + 16 * (lane >> 4)) : 0x80000000u;
+    auto store_z = [&](int t, const float (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const uint32_t off =
+            2 * t + sb < nblk ? zoff + (uint32_t)(kb + 32 * t + sb * 16) * 4 : 0x80000000u;
+        const u32x4 w = {__float_as_uint(x[sb * 4]), __float_as_uint(x[sb * 4 + 1]),
+                         __float_as_uint(x[sb * 4 + 2]), __float_as_uint(x[sb * 4 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rz, (int)off, 0, 0);
+      }
+    };
+    // two chunks in flight: ka holds even chunks, kb_ odd ones
+    KTile ka, kb_;
+    load_k(ka, 0);
+    load_k(kb_, 1);
+    for (int t = 0; t < nchunk; t += 2) {
+      float x[8];
+      scores(ka, t, x);
+      load_k(ka, t + 2);
+      store_z(t, x);
+      if (t + 1 >= nchunk) break;
+      scores(kb_, t + 1, x);
+      load_k(kb_, t + 3);
+      store_z(t + 1, x);
+    }
+    return;
+  }
+
+  // softmax / softmax1: K of chunk t+1 and V of chunk t+1 are issued while
+  // chunk t is reduced, so about two chunks stay in flight per wave
+  auto load_v = [&](u32x4 (&vr)[NV], int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const __amdgpu_buffer_rsrc_t rv = block_rsrc(vaddr, vbytes, 2 * t + sb);
+#pragma unroll
+      for (int i = 0; i < RPB; ++i) vr[sb * RPB + i] = buf_load16(rv, v_voff, i * v_step);
+    }
+  };
+  float acc[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  float m2 = -INFINITY;  // running max of this lane's head, log2 units
+  float lsum = 0.f;      // running sum over this lane's keys
+
+  KTile kt;
+  u32x4 vr[NV];
+  load_k(kt, 0);
+  load_v(vr, 0);
+  for (int t = 0; t < nchunk; ++t) {
+    float x[8];
+    scores(kt, t, x);
+    load_k(kt, t + 1);  // unconditional: past the last chunk the ranges are empty
+
+    // ---- online softmax per head (the 4 lanes with equal lane%16 share a head)
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mt = fmaxf(mt, x[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m2, mt);
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);
+    m2 = m_new;
+    lsum *= alpha;
+    // One wave per workgroup: LDS accesses of the wave complete in issue
+    // order, so the weights written here are visible to the reads below and
+    // the previous chunk's reads are done before these writes.
+    if (hh < GM) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(x[sb * 4 + r] - mref);
+          lsum += p;
+          ps[sb * 16 + 4 * (lane >> 4) + r][hh] = p;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+    }
+    // ---- weighted sum of V: lane rows ks + KS i of each block
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int kk = (i / RPB) * 16 + ks + KS * (i % RPB);
+      float vv[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        vv[2 * q] = bf_lo(vr[i][q]);
+        vv[2 * q + 1] = bf_hi(vr[i][q]);
+      }
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        const float pj = ps[kk][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pj, vv[e], acc[h][e]);
+      }
+    }
+    load_v(vr, t + 1);
+  }
+
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+#pragma unroll
+      for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      acc[h][e] = v;
     }
   }
 #pragma unroll
@@ -500,7 +776,7 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, con
     const float d = v - tauf;
     if (d > 0.f) {
       const float p = NORM == ATTN_ENTMAX15 ? d * d : d;
-      const bf16_t* vrow = vc + key_row(table, a.block_size, a.v_sb, a.v_sl, j);
+      const bf16_t* vrow = vc + key_row(table, a.block_size, a.num_blocks, a.v_sb, a.v_sl, j);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, (float)vrow[ln * DPL + e], acc[e]);
     }
@@ -521,6 +797,14 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, con
   }
 }
 
+// Page size a multiple of 16 and cache rows that fit the 32-bit buffer
+// offsets of the paged16 split kernel.
+bool paged16(const FwdArgs& a) {
+  const int64_t zbytes = (int64_t)a.G * a.max_blocks * a.block_size * 4;  // sparse z rows of a group
+  return a.block_size % 16 == 0 && a.k_sl >= a.D && a.v_sl >= a.D && a.k_sl <= (1 << 26) &&
+         a.v_sl <= (1 << 26) && zbytes < ((int64_t)1 << 31);
+}
+
 int num_splits(const FwdArgs& a) {
   const int64_t maxlen = (int64_t)a.max_blocks * a.block_size;
   return (int)((maxlen + kSplit - 1) / kSplit);
@@ -532,7 +816,18 @@ hipError_t launch_d(const FwdArgs& a, void* workspace, hipStream_t stream) {
   const int ns = num_splits(a);
   const bool cap = a.softcap > 0.f;
   dim3 g1((unsigned)((int64_t)a.B * a.Hkv * ns)), b1(64);
-  if (a.G <= 4) {
+  if (paged16(a)) {
+    if (a.G <= 4) {
+      if (cap) decode_split_paged16_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
+      else decode_split_paged16_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
+    } else if (a.G <= 8) {
+      if (cap) decode_split_paged16_kernel<D, NORM, true, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
+      else decode_split_paged16_kernel<D, NORM, false, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
+    } else {
+      if (cap) decode_split_paged16_kernel<D, NORM, true, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+      else decode_split_paged16_kernel<D, NORM, false, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+    }
+  } else if (a.G <= 4) {
     if (cap) decode_split_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
     else decode_split_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
   } else if (a.G <= 8) {

@@ -48,14 +48,14 @@ struct RowCtx {
   }
   __device__ const T* key(int j) const {
     if (a.paged) {
-      const int64_t page = table[j / a.block_size];
+      const int64_t page = page_of(table, j / a.block_size, a.num_blocks);
       return kbase + page * a.k_sb + (int64_t)(j % a.block_size) * a.k_sl;
     }
     return kbase + (int64_t)j * a.k_sl;
   }
   __device__ const T* value(int j) const {
     if (a.paged) {
-      const int64_t page = table[j / a.block_size];
+      const int64_t page = page_of(table, j / a.block_size, a.num_blocks);
       return vbase + page * a.v_sb + (int64_t)(j % a.block_size) * a.v_sl;
     }
     return vbase + (int64_t)j * a.v_sl;
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   __syncthreads();
 
   int live = a.Lk;
-  if (a.paged) live = max(0, min(a.seq_lens[b], a.max_blocks * a.block_size));
+  if (a.paged) live = paged_live(a, b);
   int lo, hi;
   key_range(i, a.Lq, live, a.causal, a.window, lo, hi);
 
