@@ -32,7 +32,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSplit = 512;      // keys per split
-constexpr int kSolveCap = 4096;  // candidate capacity of the sparse solver (LDS)
+constexpr int kSolveCap = 2048;  // candidate capacity of the sparse solver (LDS)
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -64,6 +64,141 @@ __device__ __forceinline__ int64_t key_row(const int32_t* table, int bs, int nb,
 // Partial record per (sequence, query head, split): m, l, acc[D] (fp32).
 __device__ __forceinline__ float* partial_ptr(float* ws, const FwdArgs& a, int b, int qh, int s, int ns) {
   return ws + (((int64_t)b * a.Hq + qh) * ns + s) * (a.D + 2);
+}
+
+// Threshold search step over the candidate set L = {z > t} (see the
+// prefill kernels): returns tau when the closed form over L lies below every
+// member of L (then L is the support), else a larger lower bound.
+template <int NORM>
+__device__ __forceinline__ double solve_step(double c, double s1, double s2, float mn, double mref,
+                                             double t, bool& exact) {
+  const double ty = t - mref;
+  double tcf, step;
+  bool valid;
+  if (NORM == ATTN_SPARSEMAX) {
+    tcf = (s1 - 1.0) / c;
+    valid = true;
+    step = tcf;
+  } else {
+    const double mu = s1 / c;
+    const double ss = s2 - s1 * mu;
+    const double delta = (1.0 - ss) / c;
+    valid = delta >= 0.0;
+    tcf = valid ? mu - sqrt(delta) : 0.0;
+    const double f = s2 - 2.0 * ty * s1 + c * ty * ty - 1.0;
+    const double fp = 2.0 * (s1 - c * ty);
+    step = ty + f / fp;
+  }
+  const double mny = (double)mn - mref;
+  if (valid && tcf < mny) {
+    exact = true;
+    return mref + tcf;
+  }
+  exact = false;
+  return mref + fmax(step, mny);
+}
+
+// Sparse normalizers.  The threshold of a subset of a row's keys never
+// exceeds the row's threshold (more keys need a higher tau to keep the sum at
+// one), so a lower bound on the threshold of one split's keys alone ("split
+// floor") is a lower bound on tau: every key at or below it has zero weight.
+// Per (row, split) the split kernel keeps the keys above its floor, with the
+// split's max and floor:
+//   smax, sfloor [rows][ns] f32;  cnt [rows][ns] i32;
+//   cz [rows][ns][kSplit] f32, ci [rows][ns][kSplit] u16 (key - s kSplit),
+// lists in key order; rows = B Hq.
+struct SparseLists {
+  float* smax;
+  float* sfloor;
+  int* cnt;
+  float* cz;
+  uint16_t* ci;
+};
+__device__ __forceinline__ SparseLists sparse_lists(float* ws, const FwdArgs& a, int ns) {
+  const int64_t rn = (int64_t)a.B * a.Hq * ns;
+  SparseLists l;
+  l.smax = ws;
+  l.sfloor = ws + rn;
+  l.cnt = (int*)(ws + 2 * rn);
+  l.cz = ws + 3 * rn;
+  l.ci = (uint16_t*)(ws + 3 * rn + rn * kSplit);
+  return l;
+}
+constexpr int kZPad = kSplit + 32;  // LDS row of a split's z values (chunk overhang included)
+constexpr int kFloorSteps = 4;      // threshold steps on a split's own keys
+
+// End of a sparse split, per head: the split max, a few threshold steps over
+// the split's own keys starting at (max - 1) (each step a valid lower bound,
+// or the split's exact threshold), then the keys above that floor compacted
+// in key order with ballots.  zs[h][key - s kSplit] holds z of the split's
+// keys [k_begin, k_end); mx is the lane's running max of its head
+// (lane % 16); one wave.
+template <int NORM, int GM>
+__device__ __forceinline__ void sparse_split_lists(const FwdArgs& a, float* ws, int ns, int b, int kvh,
+                                                   int s, int k_begin, int k_end, float mx,
+                                                   const float (*zs)[kZPad]) {
+  const int lane = threadIdx.x;
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const SparseLists L = sparse_lists(ws, a, ns);
+  const int lo = k_begin - s * kSplit, hi = k_end - s * kSplit;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int h = 0; h < a.G && h < GM; ++h) {
+    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h));
+    const double mref = (double)mh;
+    double t = mref - 1.0;
+    for (int it = 0; it < kFloorSteps; ++it) {
+      double c = 0.0, s1 = 0.0, s2 = 0.0;
+      float mn = INFINITY;
+      for (int idx = lo + lane; idx < hi; idx += 64) {
+        const float v = zs[h][idx];
+        if ((double)v > t) {
+          const double y = (double)v - mref;
+          c += 1.0;
+          s1 += y;
+          s2 += y * y;
+          mn = fminf(mn, v);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        c += __shfl_xor(c, o, 64);
+        s1 += __shfl_xor(s1, o, 64);
+        s2 += __shfl_xor(s2, o, 64);
+        mn = fminf(mn, __shfl_xor(mn, o, 64));
+      }
+      bool ex;
+      const double tn = solve_step<NORM>(c, s1, s2, mn, mref, t, ex);
+      if (ex) {
+        // the split's exact threshold; step below it by a rounding margin
+        t = fmax(t, tn - 1e-9 * (1.0 + fabs(tn)));
+        break;
+      }
+      t = fmax(t, tn);
+    }
+    const float tf = __double2float_rd(t);  // the floor as stored, rounded down
+    const int64_t slot = ((int64_t)b * a.Hq + (int64_t)kvh * a.G + h) * ns + s;
+    float* czp = L.cz + slot * kSplit;
+    uint16_t* cip = L.ci + slot * kSplit;
+    int count = 0;
+    for (int c0 = lo; c0 < hi; c0 += 64) {
+      const int idx = c0 + lane;
+      const float z = idx < hi ? zs[h][idx] : -INFINITY;
+      const bool f = z > tf;
+      const unsigned long long bal = __ballot(f);
+      if (f) {
+        const int pos = count + __popcll(bal & below);
+        czp[pos] = z;
+        cip[pos] = (uint16_t)idx;
+      }
+      count += __popcll(bal);
+    }
+    if (lane == 0) {
+      L.smax[slot] = mh;
+      L.sfloor[slot] = tf;
+      L.cnt[slot] = count;
+    }
+  }
 }
 
 // GM: compile-time bound on the group size G (query heads per kv head).
@@ -125,9 +260,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
   float m2 = -INFINITY;  // running max of this lane's head, log2 units
   float lsum = 0.f;      // running sum (this lane's keys only; reduced at the end)
 
-  float* zrow = (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15)
-                    ? ws + ((int64_t)b * a.Hq + qh) * ((int64_t)a.max_blocks * a.block_size)
-                    : nullptr;
+  constexpr bool SPARSE = NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15;
+  __shared__ float zs[SPARSE ? GM : 1][SPARSE ? kZPad : 1];  // z of the split, per head
+  float mx = -INFINITY;                                      // lane's running max of z
 
   for (int k0 = k_begin; k0 < k_end; k0 += 32) {
     // ---- scores of keys k0 .. k0+31 (two 16-key MFMA blocks)
@@ -172,19 +307,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
         x[sb * 4 + r] = j < k_end ? v : -INFINITY;
       }
 
-    if (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
-      // store z for the solver (16 bytes per lane and block)
-      if (head_ok) {
+    if (SPARSE) {
+      // z to LDS (k0 is not 4-aligned here: scalar stores); the rows are padded
+      // for the keys past k_end of the last chunk
+      if (hh < GM) {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const int j = k0 + sb * 16 + 4 * (lane >> 4);
-          if (j + 3 < k_end) {
-            *(f32x4*)(zrow + j) = f32x4{x[sb * 4], x[sb * 4 + 1], x[sb * 4 + 2], x[sb * 4 + 3]};
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (j + r < k_end) zrow[j + r] = x[sb * 4 + r];
-          }
+        for (int i = 0; i < 8; ++i) {
+          zs[hh][k0 - s * kSplit + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3)] = x[i];
+          mx = fmaxf(mx, x[i]);
         }
       }
       continue;
@@ -248,7 +378,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
     }
   }
 
-  if (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) return;
+  if constexpr (SPARSE) {
+    sparse_split_lists<NORM, GM>(a, ws, ns, b, kvh, s, k_begin, k_end, mx, zs);
+    return;
+  }
 
   // ---- partial record: reduce acc over the KS key slots, l over the 4 lanes of a head
   lsum += __shfl_xor(lsum, 16, 64);
@@ -412,27 +545,23 @@ __global__ __launch_bounds__(64) void decode_split_paged16_kernel(FwdArgs a, flo
   };
 
   if (SPARSE) {
-    // z rows of the group's heads behind one resource; padding heads (and
-    // the empty block past an odd block count) store out of range, which
-    // drops the store, so every store is issued unconditionally.  Keys of a
-    // real block outside [k_begin, k_end) store -inf at positions no solver
-    // reads (below the window, or up to the next multiple of 16 past the
-    // sequence end, inside the row since pages hold 16k keys).
-    const int64_t zlen = (int64_t)a.max_blocks * a.block_size;
-    const int zrow0 = __builtin_amdgcn_readfirstlane(b * a.Hq + kvh * G);  // uniform
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(ws + (int64_t)zrow0 * zlen, (uint32_t)(G * zlen * 4));
-    const uint32_t zoff = head_ok ? (uint32_t)(hh * zlen * 4 + 16 * (lane >> 4)) : 0x80000000u;
-    auto store_z = [&](int t, const float (&x)[8]) __attribute__((always_inline)) {
+    // z of the split to LDS (k0 is 16-aligned: one 16-byte store per block;
+    // the padded rows take the empty block past an odd block count), then
+    // the per-head lists.  Two chunks of K are in flight: ka holds even
+    // chunks, kb_ odd ones.
+    __shared__ float zs[GM][kZPad];
+    float mx = -INFINITY;
+    auto stage_z = [&](int t, const float (&x)[8]) __attribute__((always_inline)) {
+      if (hh < GM) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const uint32_t off =
-            2 * t + sb < nblk ? zoff + (uint32_t)(kb + 32 * t + sb * 16) * 4 : 0x80000000u;
-        const u32x4 w = {__float_as_uint(x[sb * 4]), __float_as_uint(x[sb * 4 + 1]),
-                         __float_as_uint(x[sb * 4 + 2]), __float_as_uint(x[sb * 4 + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, rz, (int)off, 0, 0);
+        for (int sb = 0; sb < 2; ++sb) {
+          const int loc = kb + 32 * t + sb * 16 + 4 * (lane >> 4) - s * kSplit;
+          *(f32x4*)&zs[hh][loc] = f32x4{x[sb * 4], x[sb * 4 + 1], x[sb * 4 + 2], x[sb * 4 + 3]};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i]);
       }
     };
-    // two chunks in flight: ka holds even chunks, kb_ odd ones
     KTile ka, kb_;
     load_k(ka, 0);
     load_k(kb_, 1);
@@ -440,12 +569,13 @@ __global__ __launch_bounds__(64) void decode_split_paged16_kernel(FwdArgs a, flo
       float x[8];
       scores(ka, t, x);
       load_k(ka, t + 2);
-      store_z(t, x);
+      stage_z(t, x);
       if (t + 1 >= nchunk) break;
       scores(kb_, t + 1, x);
       load_k(kb_, t + 3);
-      store_z(t + 1, x);
+      stage_z(t + 1, x);
     }
+    sparse_split_lists<NORM, GM>(a, ws, ns, b, kvh, s, k_begin, k_end, mx, zs);
     return;
   }
 
@@ -632,53 +762,53 @@ __device__ __forceinline__ float block_min(float v, float* red) {
   return fminf(fminf(red[0], red[1]), fminf(red[2], red[3]));
 }
 
-// Threshold search step over the candidate set L = {z > t} (see the
-// prefill kernels): returns tau when the closed form over L lies below every
-// member of L (then L is the support), else a larger lower bound.
-template <int NORM>
-__device__ __forceinline__ double solve_step(double c, double s1, double s2, float mn, double mref,
-                                             double t, bool& exact) {
-  const double ty = t - mref;
-  double tcf, step;
-  bool valid;
-  if (NORM == ATTN_SPARSEMAX) {
-    tcf = (s1 - 1.0) / c;
-    valid = true;
-    step = tcf;
-  } else {
-    const double mu = s1 / c;
-    const double ss = s2 - s1 * mu;
-    const double delta = (1.0 - ss) / c;
-    valid = delta >= 0.0;
-    tcf = valid ? mu - sqrt(delta) : 0.0;
-    const double f = s2 - 2.0 * ty * s1 + c * ty * ty - 1.0;
-    const double fp = 2.0 * (s1 - c * ty);
-    step = ty + f / fp;
+
+// Exclusive prefix sum over the 256 threads of a block; returns the block total.
+__device__ __forceinline__ int block_scan_excl(int v, int& excl, int* wtot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
-  const double mny = (double)mn - mref;
-  if (valid && tcf < mny) {
-    exact = true;
-    return mref + tcf;
-  }
-  exact = false;
-  return mref + fmax(step, mny);
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w2 = 0; w2 < w; ++w2) before += wtot[w2];
+  excl = before + incl - v;
+  const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  __syncthreads();
+  return total;
 }
 
-// One (sequence, query head) row of a sparse normalizer: threshold, then the
-// weighted sum of the support's V rows.
+// One (sequence, query head) row of a sparse normalizer.
+//  1. row max M and t0 = the largest split floor (a lower bound on tau);
+//  2. the entries above t0 of the split lists are gathered into LDS,
+//     concatenated in split order, so they stay in key order (each list
+//     holds every key of its split above t0);
+//  3. threshold search from t0 over the entries (over the lists in global
+//     memory if they outgrow LDS);
+//  4. the support's weights and V row offsets are compacted in LDS, then
+//     16-byte V chunks of several support rows are summed per wave, so V
+//     rows of zero-weight keys are never read.
 template <int D, int NORM>
-__global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, const float* ws) {
-  __shared__ float cz[kSolveCap];
-  __shared__ int ci[kSolveCap];
-  __shared__ double redd[4];
+__global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, float* ws, int ns) {
+  constexpr int LPK = D / 8;      // lanes per V row (8 dims each)
+  constexpr int KPW = 64 / LPK;   // V rows per wave and step
+  __shared__ float cz[kSolveCap];      // z, later the support weights
+  __shared__ int ci[kSolveCap];        // key index
+  __shared__ int64_t voff[kSolveCap];  // V row offsets of the support (elements)
+  __shared__ int pf[257];
+  __shared__ int wtot[4];
+  __shared__ double redd[4][3];
   __shared__ float redf[4];
   __shared__ float oacc[4][D];
 
   const int row = blockIdx.x;
   const int b = row / a.Hq, qh = row - b * a.Hq, kvh = qh / a.G;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, ln = tid & 63;
   const SeqView sv = seq_view(a, b);
-  const float* z = ws + (int64_t)row * ((int64_t)a.max_blocks * a.block_size);
   bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)qh * a.o_sh;
 
   if (sv.lo >= sv.n) {  // no visible key
@@ -689,73 +819,124 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, con
     }
     return;
   }
-  // row max
-  float m = -INFINITY;
-  for (int j = sv.lo + tid; j < sv.n; j += 256) m = fmaxf(m, z[j]);
+  // the splits holding visible keys, all of them non-empty
+  const int s0 = sv.lo / kSplit, s1 = (sv.n - 1) / kSplit;
+  const SparseLists L = sparse_lists(ws, a, ns);
+  const float* smax = L.smax + (int64_t)row * ns;
+  const int* cnt = L.cnt + (int64_t)row * ns;
+  auto list_z = [&](int s) { return L.cz + ((int64_t)row * ns + s) * kSplit; };
+  auto list_i = [&](int s) { return L.ci + ((int64_t)row * ns + s) * kSplit; };
+
+  // 1. row max and the largest split floor (tau >= every split floor)
+  const float* sfloor = L.sfloor + (int64_t)row * ns;
+  float m = -INFINITY, fl = -INFINITY;
+  for (int s = s0 + tid; s <= s1; s += 256) {
+    m = fmaxf(m, smax[s]);
+    fl = fmaxf(fl, sfloor[s]);
+  }
   m = block_max(m, redf);
+  fl = block_max(fl, redf);
   const double mref = (double)m;
-  // candidates above m - 1 (tau >= m - 1) into LDS, in key order (ballot
-  // prefix sums), so every later sum runs in a fixed order
-  __shared__ int wcnt[4];
-  double t = mref - 1.0;
+  const double t0 = (double)fl;  // every list holds all of its split's keys above t0
+
+  // 2. entries above t0 of the qualifying lists into LDS, in key order;
+  // 256 splits at a time, their entries flattened by a prefix sum over the
+  // list lengths, then compacted with ballots
   int base = 0;
-  const int wv = tid >> 6, ln0 = tid & 63;
-  for (int j0 = sv.lo; j0 < sv.n; j0 += 256) {
-    const int j = j0 + tid;
-    const float v = j < sv.n ? z[j] : -INFINITY;
-    const bool flag = (double)v > t;
-    const unsigned long long bal = __ballot(flag);
-    const int before = __popcll(bal & ((1ull << ln0) - 1ull));
-    if (ln0 == 0) wcnt[wv] = __popcll(bal);
+  for (int sb0 = s0; sb0 <= s1; sb0 += 256) {
+    const int s = sb0 + tid;
+    const int c = (s <= s1 && (double)smax[s] > t0) ? cnt[s] : 0;
+    int excl;
+    const int T = block_scan_excl(c, excl, wtot);
+    pf[tid] = excl;
+    if (tid == 0) pf[256] = T;
     __syncthreads();
-    int off = base;
-    for (int w2 = 0; w2 < wv; ++w2) off += wcnt[w2];
-    const int slot = off + before;
-    if (flag && slot < kSolveCap) {
-      cz[slot] = v;
-      ci[slot] = j;
+    for (int f0 = 0; f0 < T; f0 += 256) {
+      const int f = f0 + tid;
+      float v = -INFINITY;
+      int key = 0;
+      if (f < T) {
+        int lo = 0, hi = 256;  // last i with pf[i] <= f (that split has entries)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pf[mid] <= f) lo = mid;
+          else hi = mid;
+        }
+        const int e = f - pf[lo], sx = sb0 + lo;
+        v = list_z(sx)[e];
+        key = sx * kSplit + (int)list_i(sx)[e];
+      }
+      const bool flag = (double)v > t0;
+      const unsigned long long bal = __ballot(flag);
+      const int before = __popcll(bal & ((1ull << ln) - 1ull));
+      if (ln == 0) wtot[w] = __popcll(bal);
+      __syncthreads();
+      int off = base;
+      for (int w2 = 0; w2 < w; ++w2) off += wtot[w2];
+      if (flag && off + before < kSolveCap) {
+        cz[off + before] = v;
+        ci[off + before] = key;
+      }
+      base += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+      __syncthreads();
     }
-    base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-    __syncthreads();
   }
   const int ncand = base;
   const bool in_lds = ncand <= kSolveCap;
-  // Newton / closed form over {z > t}, on the LDS candidates or the row itself
+
+  // every list entry (z, key) of a qualifying split, threads (or waves) strided
+  auto for_lists = [&](int first, int stride, auto&& f) __attribute__((always_inline)) {
+    for (int s = s0; s <= s1; ++s) {
+      if (!((double)smax[s] > t0)) continue;
+      const int n_s = cnt[s];
+      const float* lz = list_z(s);
+      const uint16_t* li = list_i(s);
+      for (int e = first; e < n_s; e += stride) f(lz[e], s * kSplit + (int)li[e]);
+    }
+  };
+
+  // 3. Newton / closed form over {z > t}
+  double t = t0;
   double tau = INFINITY;
   double ksup = 0.0;
-  const int lim = (in_lds ? ncand : sv.n - sv.lo) + 2;
+  const int lim = ncand + 2;
   for (int it = 0; it < lim; ++it) {
-    double c = 0.0, s1 = 0.0, s2 = 0.0;
+    double c = 0.0, s1d = 0.0, s2 = 0.0;
     float mn = INFINITY;
+    auto add = [&](float v, int) __attribute__((always_inline)) {
+      if ((double)v > t) {
+        const double y = (double)v - mref;
+        c += 1.0;
+        s1d += y;
+        s2 += y * y;
+        mn = fminf(mn, v);
+      }
+    };
     if (in_lds) {
-      for (int e = tid; e < ncand; e += 256) {
-        const float v = cz[e];
-        if ((double)v > t) {
-          const double y = (double)v - mref;
-          c += 1.0;
-          s1 += y;
-          s2 += y * y;
-          mn = fminf(mn, v);
-        }
-      }
+      for (int e = tid; e < ncand; e += 256) add(cz[e], 0);
     } else {
-      for (int j = sv.lo + tid; j < sv.n; j += 256) {
-        const float v = z[j];
-        if ((double)v > t) {
-          const double y = (double)v - mref;
-          c += 1.0;
-          s1 += y;
-          s2 += y * y;
-          mn = fminf(mn, v);
-        }
-      }
+      for_lists(tid, 256, add);
     }
-    c = block_sum(c, redd);
-    s1 = block_sum(s1, redd);
-    s2 = block_sum(s2, redd);
-    mn = block_min(mn, redf);
+    for (int o = 32; o >= 1; o >>= 1) {
+      c += __shfl_xor(c, o, 64);
+      s1d += __shfl_xor(s1d, o, 64);
+      s2 += __shfl_xor(s2, o, 64);
+      mn = fminf(mn, __shfl_xor(mn, o, 64));
+    }
+    if (ln == 0) {
+      redd[w][0] = c;
+      redd[w][1] = s1d;
+      redd[w][2] = s2;
+      redf[w] = mn;
+    }
+    __syncthreads();
+    c = redd[0][0] + redd[1][0] + redd[2][0] + redd[3][0];
+    s1d = redd[0][1] + redd[1][1] + redd[2][1] + redd[3][1];
+    s2 = redd[0][2] + redd[1][2] + redd[2][2] + redd[3][2];
+    mn = fminf(fminf(redf[0], redf[1]), fminf(redf[2], redf[3]));
+    __syncthreads();
     bool ex;
-    const double tn = solve_step<NORM>(c, s1, s2, mn, mref, t, ex);
+    const double tn = solve_step<NORM>(c, s1d, s2, mn, mref, t, ex);
     if (ex) {
       tau = tn;
       ksup = c;
@@ -763,31 +944,92 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, con
     }
     t = fmax(t, tn);
   }
-  // weighted sum of V over the support: 4 waves split the keys, lanes own dims
+
+  // 4. weighted sum of the support's V rows
   const float tauf = (float)tau;
-  const int w = tid >> 6, ln = tid & 63;
-  constexpr int DPL = D / 64;  // dims per lane
-  float acc[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   const int32_t* table = a.block_table + (int64_t)b * a.max_blocks;
   const bf16_t* vc = (const bf16_t*)a.v + (int64_t)kvh * a.v_sh;
-  auto add_key = [&](int j, float v) {
-    const float d = v - tauf;
-    if (d > 0.f) {
-      const float p = NORM == ATTN_ENTMAX15 ? d * d : d;
-      const bf16_t* vrow = vc + key_row(table, a.block_size, a.num_blocks, a.v_sb, a.v_sl, j);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, (float)vrow[ln * DPL + e], acc[e]);
-    }
+  auto weight = [&](float v) __attribute__((always_inline)) {
+    const float dz = v - tauf;
+    return dz > 0.f ? (NORM == ATTN_ENTMAX15 ? dz * dz : dz) : 0.f;
   };
-  if (in_lds) {
-    for (int e = w; e < ncand; e += 4) add_key(ci[e], cz[e]);  // wave-uniform key
-  } else {
-    for (int j = sv.lo + w; j < sv.n; j += 4) add_key(j, z[j]);
-  }
+  float acc[8];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) oacc[w][ln * DPL + e] = acc[e];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const int dch = ln % LPK;
+  if (in_lds) {
+    // compact the support (weight, V row offset) in place, in key order
+    int nsup = 0;
+    for (int e0 = 0; e0 < ncand; e0 += 256) {
+      const int e = e0 + tid;
+      const float p = e < ncand ? weight(cz[e]) : 0.f;
+      const int key = e < ncand ? ci[e] : 0;
+      const bool flag = p > 0.f;
+      const unsigned long long bal = __ballot(flag);
+      const int before = __popcll(bal & ((1ull << ln) - 1ull));
+      if (ln == 0) wtot[w] = __popcll(bal);
+      __syncthreads();  // every entry of this round has been read
+      int off = nsup;
+      for (int w2 = 0; w2 < w; ++w2) off += wtot[w2];
+      if (flag) {
+        cz[off + before] = p;
+        voff[off + before] = page_of(table, key / a.block_size, a.num_blocks) * a.v_sb +
+                             (int64_t)(key % a.block_size) * a.v_sl;
+      }
+      nsup += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+      __syncthreads();
+    }
+    // LPK lanes per row, KPW rows per wave, 4 waves: rows e = slot + 4 KPW i
+    const int slot = w * KPW + ln / LPK;
+    int e = slot;
+    for (; e + 12 * KPW < nsup; e += 16 * KPW) {  // four rows in flight per lane
+      u32x4 v4[4];
+      float p4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v4[u] = *(const u32x4*)(vc + voff[e + 4 * KPW * u] + 8 * dch);
+        p4[u] = cz[e + 4 * KPW * u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(p4[u], bf_lo(v4[u][q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(p4[u], bf_hi(v4[u][q]), acc[2 * q + 1]);
+        }
+    }
+    for (; e < nsup; e += 4 * KPW) {
+      const u32x4 v = *(const u32x4*)(vc + voff[e] + 8 * dch);
+      const float p = cz[e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(p, bf_lo(v[q]), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(p, bf_hi(v[q]), acc[2 * q + 1]);
+      }
+    }
+  } else {
+    // lists outgrew LDS: the wave's lanes split one row (LPK lanes), rows by wave
+    for_lists(w * KPW + ln / LPK, 4 * KPW, [&](float v, int key) __attribute__((always_inline)) {
+      const float p = weight(v);
+      if (p > 0.f) {
+        const bf16_t* vrow = vc + key_row(table, a.block_size, a.num_blocks, a.v_sb, a.v_sl, key);
+        const u32x4 x = *(const u32x4*)(vrow + 8 * dch);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(p, bf_lo(x[q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(p, bf_hi(x[q]), acc[2 * q + 1]);
+        }
+      }
+    });
+  }
+  // reduce over the KPW row slots of the wave, then over the waves
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    for (int o = LPK; o < 64; o <<= 1) acc[q] += __shfl_xor(acc[q], o, 64);
+  if (ln < LPK) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) oacc[w][8 * ln + q] = acc[q];
+  }
   __syncthreads();
   for (int d = tid; d < D; d += 256)
     orow[d] = (bf16_t)(oacc[0][d] + oacc[1][d] + oacc[2][d] + oacc[3][d]);
@@ -843,7 +1085,7 @@ hipError_t launch_d(const FwdArgs& a, void* workspace, hipStream_t stream) {
   if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1)
     decode_combine_kernel<D, NORM><<<g2, b2, 0, stream>>>(a, ws, ns);
   else
-    decode_sparse_solve_kernel<D, NORM><<<g2, b2, 0, stream>>>(a, ws);
+    decode_sparse_solve_kernel<D, NORM><<<g2, b2, 0, stream>>>(a, ws, ns);
   return hipGetLastError();
 }
 
@@ -876,7 +1118,8 @@ bool decode_supported(const FwdArgs& a) {
 size_t decode_workspace_bytes(const FwdArgs& a) {
   if (a.norm == ATTN_SOFTMAX || a.norm == ATTN_SOFTMAX1)
     return (size_t)a.B * a.Hq * num_splits(a) * (a.D + 2) * sizeof(float);
-  return (size_t)a.B * a.Hq * ((size_t)a.max_blocks * a.block_size) * sizeof(float);
+  // split lists: max, floor, length, z and key offset per (row, split)
+  return (size_t)a.B * a.Hq * num_splits(a) * (3 * sizeof(float) + kSplit * (sizeof(float) + sizeof(uint16_t)));
 }
 
 hipError_t launch_decode(const FwdArgs& a, void* workspace, hipStream_t stream) {
