@@ -32,6 +32,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSplit = 512;      // keys per split
+static_assert((kSplit & (kSplit - 1)) == 0, "split lists store key offsets masked to the split");
 constexpr int kSolveCap = 2048;  // candidate capacity of the sparse solver (LDS)
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -125,79 +126,114 @@ __device__ __forceinline__ SparseLists sparse_lists(float* ws, const FwdArgs& a,
   return l;
 }
 constexpr int kZPad = kSplit + 32;  // LDS row of a split's z values (chunk overhang included)
-constexpr int kFloorSteps = 4;      // threshold steps on a split's own keys
+constexpr int kFloorSteps = 3;      // threshold steps on a split's own keys
 
-// End of a sparse split, per head: the split max, a few threshold steps over
-// the split's own keys starting at (max - 1) (each step a valid lower bound,
-// or the split's exact threshold), then the keys above that floor compacted
-// in key order with ballots.  zs[h][key - s kSplit] holds z of the split's
-// keys [k_begin, k_end); mx is the lane's running max of its head
-// (lane % 16); one wave.
+// End of a sparse split.  The heads of the group run side by side (64 / GP
+// lanes each, GP = G rounded up to a power of two): per head the split max
+// mh, up to kFloorSteps threshold steps in fp32 over the split's own keys
+// starting at mh - 1 (the same step as the row solver: the closed form over
+// {z > t} if it lies below that set's minimum, else a larger lower bound),
+// then the floor, lowered by a margin that covers the fp32 rounding of the
+// steps, and the keys above it compacted in key order with ballots.
+// zs[h][key - s kSplit] holds z of the split's keys [k_begin, k_end); mx is
+// the lane's running max of its head (lane % 16); one wave.
 template <int NORM, int GM>
 __device__ __forceinline__ void sparse_split_lists(const FwdArgs& a, float* ws, int ns, int b, int kvh,
                                                    int s, int k_begin, int k_end, float mx,
-                                                   const float (*zs)[kZPad]) {
-  const int lane = threadIdx.x;
+                                                   float (*zs)[kZPad], uint16_t (*zi)[kSplit]) {
+  const int lane = threadIdx.x & 63;
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   const SparseLists L = sparse_lists(ws, a, ns);
   const int lo = k_begin - s * kSplit, hi = k_end - s * kSplit;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int h = 0; h < a.G && h < GM; ++h) {
-    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h));
-    const double mref = (double)mh;
-    double t = mref - 1.0;
-    for (int it = 0; it < kFloorSteps; ++it) {
-      double c = 0.0, s1 = 0.0, s2 = 0.0;
-      float mn = INFINITY;
-      for (int idx = lo + lane; idx < hi; idx += 64) {
-        const float v = zs[h][idx];
-        if ((double)v > t) {
-          const double y = (double)v - mref;
-          c += 1.0;
+  const int G = min(a.G, GM);
+  int gp = 1;
+  while (gp < G) gp <<= 1;
+  const int lph = 64 / gp;                 // lanes per head
+  const int h = lane / lph, sub = lane - h * lph;
+  const bool act = h < G;
+  const int hr = act ? h : 0;
+  const float mh = __shfl(mx, hr, 64);     // lane h holds head h's max
+  float t = mh - 1.0f;
+  bool done = false;
+  for (int it = 0; it < kFloorSteps; ++it) {
+    float c = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
+    if (!done) {
+      for (int idx = lo + sub; idx < hi; idx += lph) {
+        const float v = zs[hr][idx];
+        if (v > t) {
+          const float y = v - mh;
+          c += 1.f;
           s1 += y;
-          s2 += y * y;
+          s2 = fmaf(y, y, s2);
           mn = fminf(mn, v);
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        c += __shfl_xor(c, o, 64);
-        s1 += __shfl_xor(s1, o, 64);
-        s2 += __shfl_xor(s2, o, 64);
-        mn = fminf(mn, __shfl_xor(mn, o, 64));
-      }
-      bool ex;
-      const double tn = solve_step<NORM>(c, s1, s2, mn, mref, t, ex);
-      if (ex) {
-        // the split's exact threshold; step below it by a rounding margin
-        t = fmax(t, tn - 1e-9 * (1.0 + fabs(tn)));
-        break;
-      }
-      t = fmax(t, tn);
     }
-    const float tf = __double2float_rd(t);  // the floor as stored, rounded down
-    const int64_t slot = ((int64_t)b * a.Hq + (int64_t)kvh * a.G + h) * ns + s;
-    float* czp = L.cz + slot * kSplit;
-    uint16_t* cip = L.ci + slot * kSplit;
-    int count = 0;
-    for (int c0 = lo; c0 < hi; c0 += 64) {
-      const int idx = c0 + lane;
-      const float z = idx < hi ? zs[h][idx] : -INFINITY;
-      const bool f = z > tf;
-      const unsigned long long bal = __ballot(f);
-      if (f) {
-        const int pos = count + __popcll(bal & below);
-        czp[pos] = z;
-        cip[pos] = (uint16_t)idx;
+    for (int o = 1; o < lph; o <<= 1) {  // sums over the head's lanes
+      c += __shfl_xor(c, o, 64);
+      s1 += __shfl_xor(s1, o, 64);
+      s2 += __shfl_xor(s2, o, 64);
+      mn = fminf(mn, __shfl_xor(mn, o, 64));
+    }
+    if (!done && c > 0.f) {
+      float tcf, step;
+      bool valid;
+      if (NORM == ATTN_SPARSEMAX) {
+        tcf = (s1 - 1.f) / c;
+        valid = true;
+        step = tcf;
+      } else {
+        const float mu = s1 / c;
+        const float delta = (1.f - (s2 - s1 * mu)) / c;
+        valid = delta >= 0.f;
+        tcf = valid ? mu - sqrtf(delta) : 0.f;
+        const float ty = t - mh;
+        const float f = s2 - 2.f * ty * s1 + c * ty * ty - 1.f;
+        const float fp = 2.f * (s1 - c * ty);
+        step = ty + f / fp;
       }
-      count += __popcll(bal);
+      const float mny = mn - mh;
+      if (valid && tcf < mny) {
+        t = mh + tcf;
+        done = true;
+      } else {
+        t = fmaxf(t, mh + fmaxf(step, mny));
+      }
     }
-    if (lane == 0) {
-      L.smax[slot] = mh;
-      L.sfloor[slot] = tf;
-      L.cnt[slot] = count;
+  }
+  const float tf = t - (1e-2f + 1e-5f * fabsf(mh));  // fp32 rounding margin
+  // compact in LDS, in place (an entry moves to a position at or below the
+  // one it was read from, and every read of a round precedes its writes),
+  // then copy the list out with contiguous stores
+  const unsigned long long grp = (lph == 64 ? ~0ull : ((1ull << lph) - 1ull)) << (h * lph);
+  const unsigned long long below = grp & ((1ull << lane) - 1ull);
+  int count = 0;
+  for (int c0 = lo; c0 < hi; c0 += lph) {
+    const int idx = c0 + sub;
+    const float z = (act && idx < hi) ? zs[hr][idx] : -INFINITY;
+    const bool f = z > tf;
+    const unsigned long long bal = __ballot(f);
+    if (f) {
+      const int pos = count + __popcll(bal & below);
+      zs[hr][pos] = z;
+      zi[hr][pos] = (uint16_t)idx;
     }
+    count += __popcll(bal & grp);
+  }
+  const int64_t slot = ((int64_t)b * a.Hq + (int64_t)kvh * a.G + hr) * ns + s;
+  float* czp = L.cz + slot * kSplit;
+  uint16_t* cip = L.ci + slot * kSplit;
+  if (act) {
+    for (int e = sub; e < count; e += lph) {
+      czp[e] = zs[hr][e];
+      cip[e] = zi[hr][e];
+    }
+  }
+  if (act && sub == 0) {
+    L.smax[slot] = mh;
+    L.sfloor[slot] = tf;
+    L.cnt[slot] = count;
   }
 }
 
@@ -262,6 +298,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
 
   constexpr bool SPARSE = NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15;
   __shared__ float zs[SPARSE ? GM : 1][SPARSE ? kZPad : 1];  // z of the split, per head
+  __shared__ uint16_t zi[SPARSE ? GM : 1][SPARSE ? kSplit : 1];  // list key offsets
   float mx = -INFINITY;                                      // lane's running max of z
 
   for (int k0 = k_begin; k0 < k_end; k0 += 32) {
@@ -379,7 +416,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
   }
 
   if constexpr (SPARSE) {
-    sparse_split_lists<NORM, GM>(a, ws, ns, b, kvh, s, k_begin, k_end, mx, zs);
+    sparse_split_lists<NORM, GM>(a, ws, ns, b, kvh, s, k_begin, k_end, mx, zs, zi);
     return;
   }
 
@@ -430,20 +467,29 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // 32-key chunk and V of the current one are in flight while the current
 // chunk's scores, weights and PV sum are computed.
 template <int D, int NORM, bool CAP, int GM>
-__global__ __launch_bounds__(64) void decode_split_paged16_kernel(FwdArgs a, float* ws, int ns) {
+__global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, float* ws, int ns) {
   constexpr bool SPARSE = NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15;
   constexpr int NKC = D / 32;     // k-steps of the 16x16x32 QK product
   constexpr int CPR = D / 8;      // 16-byte chunks per row
   constexpr int KS = 64 / CPR;    // key rows per PV step (lanes per chunk column)
   constexpr int RPB = 16 / KS;    // V rows per lane per 16-key block
   constexpr int NV = 32 / KS;     // V rows per lane per 32-key chunk
-  __shared__ float ps[32][GM];    // weights of the chunk's keys, per head
 
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x % ns;
-  const int bh = blockIdx.x / ns;
-  const int kvh = bh % a.Hkv;
-  const int b = bh / a.Hkv;
+  // A workgroup is WPG waves on WPG consecutive kv heads of one split, so the
+  // slot rows of a page (all heads side by side) are read together; the
+  // waves never synchronize.  Dynamic LDS: per wave the chunk's weights
+  // [32][GM]; sparse: per wave the split's z values [GM][kZPad], then per
+  // wave the list key offsets [GM][kSplit] (u16).
+  extern __shared__ float dyn_lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wpg = blockDim.x >> 6;
+  const int ngrp = a.Hkv / wpg;
+  const int kvh = (blockIdx.x % ngrp) * wpg + wave;
+  const int bs_ = blockIdx.x / ngrp;
+  const int s = bs_ % ns;
+  const int b = bs_ / ns;
+  float (*ps)[GM] = (float (*)[GM])(dyn_lds + wave * 32 * GM);
   const int G = a.G;
   const SeqView sv = seq_view(a, b);
   const int k_begin = max(sv.lo, s * kSplit);
@@ -549,7 +595,9 @@ __global__ __launch_bounds__(64) void decode_split_paged16_kernel(FwdArgs a, flo
     // the padded rows take the empty block past an odd block count), then
     // the per-head lists.  Two chunks of K are in flight: ka holds even
     // chunks, kb_ odd ones.
-    __shared__ float zs[GM][kZPad];
+    float (*zs)[kZPad] = (float (*)[kZPad])(dyn_lds + wpg * 32 * GM + wave * GM * kZPad);
+    uint16_t (*zi)[kSplit] =
+        (uint16_t (*)[kSplit])(dyn_lds + wpg * (32 * GM + GM * kZPad)) + wave * GM;
     float mx = -INFINITY;
     auto stage_z = [&](int t, const float (&x)[8]) __attribute__((always_inline)) {
       if (hh < GM) {
@@ -575,7 +623,7 @@ __global__ __launch_bounds__(64) void decode_split_paged16_kernel(FwdArgs a, flo
       load_k(kb_, t + 3);
       stage_z(t + 1, x);
     }
-    sparse_split_lists<NORM, GM>(a, ws, ns, b, kvh, s, k_begin, k_end, mx, zs);
+    sparse_split_lists<NORM, GM>(a, ws, ns, b, kvh, s, k_begin, k_end, mx, zs, zi);
     return;
   }
 
@@ -845,7 +893,7 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, flo
   int base = 0;
   for (int sb0 = s0; sb0 <= s1; sb0 += 256) {
     const int s = sb0 + tid;
-    const int c = (s <= s1 && (double)smax[s] > t0) ? cnt[s] : 0;
+    const int c = (s <= s1 && (double)smax[s] > t0) ? min(max(cnt[s], 0), kSplit) : 0;
     int excl;
     const int T = block_scan_excl(c, excl, wtot);
     pf[tid] = excl;
@@ -864,7 +912,7 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, flo
         }
         const int e = f - pf[lo], sx = sb0 + lo;
         v = list_z(sx)[e];
-        key = sx * kSplit + (int)list_i(sx)[e];
+        key = min(sx * kSplit + ((int)list_i(sx)[e] & (kSplit - 1)), sv.n - 1);
       }
       const bool flag = (double)v > t0;
       const unsigned long long bal = __ballot(flag);
@@ -888,10 +936,11 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, flo
   auto for_lists = [&](int first, int stride, auto&& f) __attribute__((always_inline)) {
     for (int s = s0; s <= s1; ++s) {
       if (!((double)smax[s] > t0)) continue;
-      const int n_s = cnt[s];
+      const int n_s = min(max(cnt[s], 0), kSplit);
       const float* lz = list_z(s);
       const uint16_t* li = list_i(s);
-      for (int e = first; e < n_s; e += stride) f(lz[e], s * kSplit + (int)li[e]);
+      for (int e = first; e < n_s; e += stride)
+        f(lz[e], min(s * kSplit + ((int)li[e] & (kSplit - 1)), sv.n - 1));
     }
   };
 
@@ -1059,16 +1108,29 @@ hipError_t launch_d(const FwdArgs& a, void* workspace, hipStream_t stream) {
   const bool cap = a.softcap > 0.f;
   dim3 g1((unsigned)((int64_t)a.B * a.Hkv * ns)), b1(64);
   if (paged16(a)) {
-    if (a.G <= 4) {
-      if (cap) decode_split_paged16_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
-      else decode_split_paged16_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
-    } else if (a.G <= 8) {
-      if (cap) decode_split_paged16_kernel<D, NORM, true, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
-      else decode_split_paged16_kernel<D, NORM, false, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
-    } else {
-      if (cap) decode_split_paged16_kernel<D, NORM, true, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
-      else decode_split_paged16_kernel<D, NORM, false, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
-    }
+    const int gm = a.G <= 4 ? 4 : a.G <= 8 ? 8 : 16;
+    const bool sparse = NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15;
+    auto lds_bytes = [&](int w) {
+      return (size_t)w * ((32 * gm + (sparse ? gm * kZPad : 0)) * sizeof(float) +
+                          (sparse ? gm * kSplit * sizeof(uint16_t) : 0));
+    };
+    // waves (kv heads) per workgroup: divides Hkv, LDS leaves room for two
+    // groups; the sparse kernels (LDS-heavy) measured best with two
+    int wpg = sparse ? 2 : 8;
+    while (wpg > 1 && (a.Hkv % wpg != 0 || lds_bytes(wpg) > 80 * 1024)) wpg >>= 1;
+    const size_t lds = lds_bytes(wpg);
+    dim3 g16((unsigned)((int64_t)a.B * ns * (a.Hkv / wpg))), b16(64 * wpg);
+    auto go = [&](auto kern) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      kern<<<g16, b16, lds, stream>>>(a, ws, ns);
+      return hipSuccess;
+    };
+    hipError_t e0;
+    if (gm == 4) e0 = cap ? go(decode_split_paged16_kernel<D, NORM, true, 4>) : go(decode_split_paged16_kernel<D, NORM, false, 4>);
+    else if (gm == 8) e0 = cap ? go(decode_split_paged16_kernel<D, NORM, true, 8>) : go(decode_split_paged16_kernel<D, NORM, false, 8>);
+    else e0 = cap ? go(decode_split_paged16_kernel<D, NORM, true, 16>) : go(decode_split_paged16_kernel<D, NORM, false, 16>);
+    if (e0 != hipSuccess) return e0;
   } else if (a.G <= 4) {
     if (cap) decode_split_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
     else decode_split_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
