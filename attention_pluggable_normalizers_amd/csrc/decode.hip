@@ -62,9 +62,10 @@ __device__ __forceinline__ int64_t key_row(const int32_t* table, int bs, int nb,
   return page * sb + (int64_t)(j % bs) * sl;
 }
 
-// Partial record per (sequence, query head, split): m, l, acc[D] (fp32).
+// Partial record per (sequence, query head, split): m, l, 2 pad, acc[D] (fp32;
+// acc 16-byte aligned).
 __device__ __forceinline__ float* partial_ptr(float* ws, const FwdArgs& a, int b, int qh, int s, int ns) {
-  return ws + (((int64_t)b * a.Hq + qh) * ns + s) * (a.D + 2);
+  return ws + (((int64_t)b * a.Hq + qh) * ns + s) * (a.D + 4);
 }
 
 // Threshold search step over the candidate set L = {z > t} (see the
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
     if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1) {
       for (int h = 0; h < G; ++h) {
         float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
-        for (int d = lane; d < D + 2; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
+        for (int d = lane; d < D + 4; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
       }
     }
     return;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
     }
     if (ks == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pp[2 + 8 * ch + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) pp[4 + 8 * ch + e] = acc[h][e];
     }
   }
 }
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
     if (!SPARSE) {
       for (int h = 0; h < G; ++h) {
         float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
-        for (int d = lane; d < D + 2; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
+        for (int d = lane; d < D + 4; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
       }
     }
     return;
@@ -727,21 +728,28 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
     }
     if (ks == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pp[2 + 8 * ch + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) pp[4 + 8 * ch + e] = acc[h][e];
     }
   }
 }
 
 // Merge the split partials of one (sequence, query head).  All in log2 units.
+// The block's threads form NG groups of D/4 lanes; group g sums the float4
+// chunks of splits g, g + NG, ..., then the groups are added through LDS.
 template <int D, int NORM>
 __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const float* ws, int ns) {
-  const int row = blockIdx.x;  // b * Hq + qh
+  constexpr int CH = D / 4;      // float4 chunks of acc
+  constexpr int NG = 256 / CH;   // split groups
+  constexpr int REC = D + 4;     // record stride (floats)
+  const int row = blockIdx.x;    // b * Hq + qh
   const int b = row / a.Hq, qh = row - b * a.Hq;
   const int tid = threadIdx.x;
   __shared__ float red[256];
+  __shared__ f32x4 part[NG][CH];
+  const float* rec = ws + (int64_t)row * ns * REC;
   // global max over the splits (softmax1 also counts its logit-0 sink)
   float m = -INFINITY;
-  for (int s = tid; s < ns; s += 256) m = fmaxf(m, ws[((int64_t)row * ns + s) * (D + 2)]);
+  for (int s = tid; s < ns; s += 256) m = fmaxf(m, rec[(int64_t)s * REC]);
   red[tid] = m;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -754,7 +762,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
   const float mref = M == -INFINITY ? 0.f : M;
   float l = 0.f;
   for (int s = tid; s < ns; s += 256) {
-    const float* pp = ws + ((int64_t)row * ns + s) * (D + 2);
+    const float* pp = rec + (int64_t)s * REC;
     l += pp[1] * __builtin_amdgcn_exp2f(pp[0] - mref);
   }
   red[tid] = l;
@@ -766,15 +774,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
   float L = red[0];
   if (NORM == ATTN_SOFTMAX1) L += __builtin_amdgcn_exp2f(-mref);  // the "+1" at logit 0
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  // weighted sum of the acc chunks
+  const int g = tid / CH, c = tid - g * CH;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = g; s < ns; s += NG) {
+    const float* pp = rec + (int64_t)s * REC;
+    const float w = __builtin_amdgcn_exp2f(pp[0] - mref);
+    const f32x4 v = *(const f32x4*)(pp + 4 + 4 * c);
+    acc += w * v;
+  }
+  part[g][c] = acc;
+  __syncthreads();
   bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)qh * a.o_sh;
-  for (int d = tid; d < D; d += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float* pp = ws + ((int64_t)row * ns + s) * (D + 2);
-      const float w = __builtin_amdgcn_exp2f(pp[0] - mref);
-      acc = fmaf(w, pp[2 + d], acc);
-    }
-    orow[d] = (bf16_t)(acc * inv);
+  if (tid < CH) {
+    f32x4 t = part[0][tid];
+#pragma unroll
+    for (int g2 = 1; g2 < NG; ++g2) t += part[g2][tid];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[4 * tid + e] = (bf16_t)(t[e] * inv);
   }
   if (a.stats && tid == 0) {
     float* st = a.stats + (int64_t)row * 2;
@@ -1179,7 +1196,7 @@ bool decode_supported(const FwdArgs& a) {
 
 size_t decode_workspace_bytes(const FwdArgs& a) {
   if (a.norm == ATTN_SOFTMAX || a.norm == ATTN_SOFTMAX1)
-    return (size_t)a.B * a.Hq * num_splits(a) * (a.D + 2) * sizeof(float);
+    return (size_t)a.B * a.Hq * num_splits(a) * (a.D + 4) * sizeof(float);
   // split lists: max, floor, length, z and key offset per (row, split)
   return (size_t)a.B * a.Hq * num_splits(a) * (3 * sizeof(float) + kSplit * (sizeof(float) + sizeof(uint16_t)));
 }
