@@ -702,10 +702,17 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   float floor_f = -INFINITY;  // largest float <= floor_
   int cnt = 0;                // this lane's candidates
   bool ovf = !row_ok;         // row left to the extra passes (or no row at all)
+  bool settled = false;       // floor has reached the exact threshold of the keys seen once
 
+  // Raises the floors until every row has room for a full block in both of
+  // its lanes or its floor is the exact threshold of the keys seen so far
+  // (then the buffer holds their support only, after one more compaction);
+  // at most kRefloorSteps steps.  Wave-uniform: every lane takes part
+  // (partner exchanges inside).
+  constexpr int kRefloorSteps = 8;
   auto refloor = [&]() __attribute__((always_inline)) {
-    // wave-uniform: every lane takes part (partner exchanges inside)
-    for (int it = 0; it < 8; ++it) {
+    bool done_ = ovf;
+    for (int it = 0; it < kRefloorSteps; ++it) {
       double c, s1, s2;
       float mn;
       scan_buf<SCAP>(buf, cnt, floor_, (double)mrun, c, s1, s2, mn);
@@ -713,18 +720,21 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       s1 += partner_d(s1);
       s2 += partner_d(s2);
       mn = fminf(mn, partner(mn));
-      if (!ovf && c > 0.0) {
+      bool fresh = false;
+      if (!done_ && c > 0.0) {
         bool ex;
         const double tn = thr_step<NORM>(c, s1, s2, mn, (double)mrun, floor_, ex);
         floor_ = fmax(floor_, tn);
         floor_f = float_floor(floor_);
+        done_ = fresh = ex;
+        settled = settled || ex;
+      } else {
+        done_ = true;
       }
       const int pc = partner_i(cnt);
-      const bool need = !ovf && (cnt + 16 > SCAP || pc + 16 > SCAP);
+      const bool need = (cnt + 16 > SCAP || pc + 16 > SCAP) && (!done_ || fresh);
       if (!__any(need)) break;
     }
-    const int pc = partner_i(cnt);
-    if (cnt + 16 > SCAP || pc + 16 > SCAP) ovf = true;
   };
 
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
@@ -775,13 +785,33 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             z[r] = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
             na += z[r] > floor_f ? 1 : 0;
           }
-          if (__any(!ovf && cnt + 16 > SCAP)) refloor();
-          if (!ovf && na > 0) {
+          // refloor when a lane cannot take the block, and, until the floor
+          // has once been exact, already when a lane lacks room for a full block
+          if (__any(!ovf && (cnt + na > SCAP || (!settled && cnt + 16 > SCAP)))) {
+            refloor();
+            na = 0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              if (z[r] > floor_f) {
+            for (int r = 0; r < 16; ++r) na += z[r] > floor_f ? 1 : 0;
+          }
+          // a row whose lanes cannot take the block goes to the extra passes
+          const int full = (!ovf && cnt + na > SCAP) ? 1 : 0;
+          if (__any(full)) ovf = ovf || (full | partner_i(full)) != 0;
+          if (!ovf && na > 0) {
+            if (cnt + 16 <= SCAP) {
+              // branch-free: every value is written at the append position,
+              // which only advances for the accepted ones
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
                 buf[cnt * 64] = z[r];
-                ++cnt;
+                cnt += z[r] > floor_f ? 1 : 0;
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                if (z[r] > floor_f) {
+                  buf[cnt * 64] = z[r];
+                  ++cnt;
+                }
               }
             }
           }
@@ -820,11 +850,18 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   }
   if (!done) pending = true;  // cannot happen (each step drops a candidate); kept as a guard
 
-  // ---- extra passes for rows whose support outgrew the buffer --------------
+  // ---- extra passes for rows whose candidates outgrew the buffer -----------
+  // Each pass re-streams the K tiles and, for every pending row, both
+  // accumulates (count, sums, minimum) above the floor and collects the
+  // values above it into the lane buffers.  When both halves fit, the row is
+  // solved exactly from the buffers as above; otherwise the totals give one
+  // threshold step and the next pass starts from the raised floor.
   while (__syncthreads_or(pending)) {
     double c = 0.0, s1 = 0.0, s2 = 0.0;
     float mn = INFINITY;
     const double mref = (double)mrun;
+    cnt = 0;
+    int fits = pending ? 1 : 0;
     if (t0 < t1) {
       tiles.load_k(rk, t0 * C::BN);
       tiles.store_k(kl0, tid);
@@ -840,6 +877,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         f32x16 s[C::NKB];
         qk_tile<C>(kl, qreg, l32, g, s);
         const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+        float zz[C::NKB][16];
         if (pending) {
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) {
@@ -850,12 +888,31 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
                 const int key = s_key(k0, kb, r, g);
                 if (key < mine.lo || key >= mine.hi) z = -INFINITY;
               }
+              zz[kb][r] = z;
               if ((double)z > floor_) {
                 const double y = (double)z - mref;
                 c += 1.0;
                 s1 += y;
                 s2 += y * y;
                 mn = fminf(mn, z);
+              }
+            }
+          }
+        }
+        if (__any(pending && fits)) {
+          if (pending && fits) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                if ((double)zz[kb][r] > floor_) {
+                  if (cnt < SCAP) {
+                    buf[cnt * 64] = zz[kb][r];
+                    ++cnt;
+                  } else {
+                    fits = 0;
+                  }
+                }
               }
             }
           }
@@ -868,7 +925,8 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     s1 += partner_d(s1);
     s2 += partner_d(s2);
     mn = fminf(mn, partner(mn));
-    if (pending) {
+    fits = fits & partner_i(fits);
+    if (pending && !fits) {
       bool ex;
       const double tn = thr_step<NORM>(c, s1, s2, mn, mref, floor_, ex);
       if (ex) {
@@ -877,6 +935,30 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         pending = false;
       } else {
         floor_ = fmax(floor_, tn);
+      }
+    }
+    if (!pending) cnt = 0;
+    bool solving = pending && fits;
+    for (int it = 0; it < 2 * SCAP + 4; ++it) {
+      if (!__any(solving)) break;
+      double cc, a1, a2;
+      float m1;
+      scan_buf<SCAP>(buf, cnt, floor_, mref, cc, a1, a2, m1);
+      cc += partner_d(cc);
+      a1 += partner_d(a1);
+      a2 += partner_d(a2);
+      m1 = fminf(m1, partner(m1));
+      if (solving) {
+        bool ex;
+        const double tn = thr_step<NORM>(cc, a1, a2, m1, mref, floor_, ex);
+        if (ex) {
+          tau = tn;
+          ksup = (int)cc;
+          solving = false;
+          pending = false;
+        } else {
+          floor_ = fmax(floor_, tn);
+        }
       }
     }
   }
