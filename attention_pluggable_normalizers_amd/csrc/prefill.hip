@@ -38,9 +38,12 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D_, int BN_, int NW_>
+template <int D_, int BN_, int NW_, bool PIPE_ = false>
 struct Cfg {
   static constexpr int D = D_, BN = BN_, NW = NW_;
+  // softmax family: three LDS tile buffers, and the scores of tile t + 1 are
+  // computed before the weights of tile t (matrix cores and vector ALUs overlap)
+  static constexpr bool PIPE = PIPE_;
   static constexpr int NT = NW * 64;          // threads per workgroup
   static constexpr int BM = NW * 32;          // query rows per workgroup
   static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
@@ -316,9 +319,8 @@ constexpr float kRescale = 8.f;
 
 template <class C, int NORM, bool CAP>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * C::BN * C::D];
-  bf16_t* const kl0 = lds;
-  bf16_t* const vl0 = lds + 2 * C::BN * C::D;
+  constexpr int NBUF = C::PIPE ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NBUF * 2 * C::BN * C::D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -340,6 +342,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const int klo = first.lo, khi = last.hi;
   const int t0 = klo / C::BN;
   const int t1 = khi > klo ? (khi + C::BN - 1) / C::BN : t0;
+  // LDS buffer of tile u: K [BN][D] then V^T [D][BN]
+  auto kl_of = [&](int u) { return lds + ((u - t0) % NBUF) * 2 * C::BN * C::D; };
+  auto vl_of = [&](int u) { return lds + ((u - t0) % NBUF) * 2 * C::BN * C::D + C::BN * C::D; };
 
   // this wave's rows and this lane's row
   const int wq0 = q0 + 32 * wave;
@@ -350,6 +355,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const int myq = wq0 + l32;
   const bool row_ok = myq < Lq;
   const RowBounds mine = row_bounds(row_ok ? myq : wq1, Lq, Lk, a.causal, a.window);
+  auto tile_active = [&](int t) {
+    const int k0 = t * C::BN;
+    return wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+  };
 
   bf16x8 qreg[C::NQC];
   {
@@ -370,92 +379,119 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
   const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;
 
+  // weights of one tile from its raw scores s, then O += V^T P^T
+  auto consume = [&](f32x16 (&s)[C::NKB], int t) __attribute__((always_inline)) {
+    const int k0 = t * C::BN;
+    const bf16_t* vl = vl_of(t);
+    constexpr bool kPreV = VOps<C>::N <= 8;  // V operands fit in registers across the softmax
+    VOps<C> vo;
+    if constexpr (kPreV) vo.read(vl, l32, g);
+    if (CAP) {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = capped_log2(s[kb][r], sc_over_cap, cap_log2e);
+    }
+    if ((k0 + C::BN > wfirst.hi) || (k0 < wlast.lo)) {  // tile straddles a mask bound
+      const int base = k0 + 4 * g - mine.lo;
+      const unsigned span = (unsigned)(mine.hi - mine.lo);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+          s[kb][r] = off < span ? s[kb][r] : -INFINITY;
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = pair_max(mt);
+    const float mt2 = CAP ? mt : mt * c2;
+    m_true = fmaxf(m_true, mt2);
+    const bool need = mt2 > m_use + kRescale;
+    if (__any(need)) {
+      // lanes that do not need it keep their reference (alpha = 1); a lane
+      // whose reference is still -inf gets alpha = 0 (nothing accumulated yet)
+      const float m_new = need ? mt2 : m_use;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
+      m_use = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+    }
+    const float mref = m_use == -INFINITY ? 0.f : m_use;
+    float ps = 0.f;
+    bf16x8 pk[2 * C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - mref)
+                   : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -mref));
+        ps += p[r];
+      }
+      pk[2 * kb] = p_operand(p);
+      pk[2 * kb + 1] = p_operand(p + 8);
+    }
+    lsum += ps;
+    if constexpr (kPreV)
+      pv_tile_ops<C>(vo, pk, o);
+    else
+      pv_tile<C>(vl, pk, l32, g, o);
+  };
+
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
   Tiles<C> tiles;
   tiles.init(a.k_sl, a.v_sl, tid);
-  if (t0 < t1) {
-    tiles.load(rk, rv, t0 * C::BN);
-    tiles.store(kl0, vl0, tid);
-  }
-  __syncthreads();
 
-  for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    const bf16_t* kl = kl0 + cur * C::BN * C::D;
-    const bf16_t* vl = vl0 + cur * C::BN * C::D;
-    if (t + 1 < t1) tiles.load(rk, rv, (t + 1) * C::BN);
-    const int k0 = t * C::BN;
-    const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
-    if (active) {
-      f32x16 s[C::NKB];
-      qk_tile<C>(kl, qreg, l32, g, s);
-      constexpr bool kPreV = VOps<C>::N <= 8;  // V operands fit in registers across the softmax
-      VOps<C> vo;
-      if constexpr (kPreV) vo.read(vl, l32, g);
-      if (CAP) {
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] = capped_log2(s[kb][r], sc_over_cap, cap_log2e);
-      }
-      if ((k0 + C::BN > wfirst.hi) || (k0 < wlast.lo)) {  // tile straddles a mask bound
-        const int base = k0 + 4 * g - mine.lo;
-        const unsigned span = (unsigned)(mine.hi - mine.lo);
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
-            s[kb][r] = off < span ? s[kb][r] : -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = pair_max(mt);
-      const float mt2 = CAP ? mt : mt * c2;
-      m_true = fmaxf(m_true, mt2);
-      const bool need = mt2 > m_use + kRescale;
-      if (__any(need)) {
-        // lanes that do not need it keep their reference (alpha = 1); a lane
-        // whose reference is still -inf gets alpha = 0 (nothing accumulated yet)
-        const float m_new = need ? mt2 : m_use;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
-        m_use = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
-      }
-      const float mref = m_use == -INFINITY ? 0.f : m_use;
-      float ps = 0.f;
-      bf16x8 pk[2 * C::NKB];
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - mref)
-                     : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -mref));
-          ps += p[r];
-        }
-        pk[2 * kb] = p_operand(p);
-        pk[2 * kb + 1] = p_operand(p + 8);
-      }
-      lsum += ps;
-      if constexpr (kPreV)
-        pv_tile_ops<C>(vo, pk, o);
-      else
-        pv_tile<C>(vl, pk, l32, g, o);
-    }
-    if (t + 1 < t1) {
-      bf16_t* kln = kl0 + (cur ^ 1) * C::BN * C::D;
-      bf16_t* vln = vl0 + (cur ^ 1) * C::BN * C::D;
-      tiles.store(kln, vln, tid);
+  if constexpr (!C::PIPE) {
+    if (t0 < t1) {
+      tiles.load(rk, rv, t0 * C::BN);
+      tiles.store(kl_of(t0), vl_of(t0), tid);
     }
     __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+      if (t + 1 < t1) tiles.load(rk, rv, (t + 1) * C::BN);
+      if (tile_active(t)) {
+        f32x16 s[C::NKB];
+        qk_tile<C>(kl_of(t), qreg, l32, g, s);
+        consume(s, t);
+      }
+      if (t + 1 < t1) tiles.store(kl_of(t + 1), vl_of(t + 1), tid);
+      __syncthreads();
+    }
+  } else {
+    // tiles t and t + 1 are in LDS while tile t + 2 is loaded; the scores of
+    // tile t + 1 are issued to the matrix cores before tile t's weights are
+    // computed on the vector ALUs.  Buffer of tile t + 2 = that of tile t - 1,
+    // whose last reads (its V) precede the barrier ending step t - 1.
+    for (int u = t0; u < min(t0 + 2, t1); ++u) {
+      tiles.load(rk, rv, u * C::BN);
+      tiles.store(kl_of(u), vl_of(u), tid);
+    }
+    __syncthreads();
+    f32x16 sa[C::NKB], sb[C::NKB];
+    bool act_a = t0 < t1 && tile_active(t0), act_b = false;
+    if (act_a) qk_tile<C>(kl_of(t0), qreg, l32, g, sa);
+    auto step = [&](f32x16 (&cur)[C::NKB], bool act_cur, f32x16 (&nxt)[C::NKB], bool& act_nxt, int t)
+        __attribute__((always_inline)) {
+      if (t + 2 < t1) tiles.load(rk, rv, (t + 2) * C::BN);
+      act_nxt = t + 1 < t1 && tile_active(t + 1);
+      if (act_nxt) qk_tile<C>(kl_of(t + 1), qreg, l32, g, nxt);
+      if (act_cur) consume(cur, t);
+      if (t + 2 < t1) tiles.store(kl_of(t + 2), vl_of(t + 2), tid);
+      __syncthreads();
+    };
+    for (int t = t0; t < t1; t += 2) {
+      step(sa, act_a, sb, act_b, t);
+      if (t + 1 >= t1) break;
+      step(sb, act_b, sa, act_a, t + 1);
+    }
   }
 
   // epilogue
@@ -645,6 +681,25 @@ __device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double 
   cnt = w;
 }
 
+// Keeps this lane's candidates above t (compacting them in place).
+template <int SCAP>
+__device__ __forceinline__ void compact_buf(float* buf, int& cnt, float t) {
+  int w = 0;
+  for (int e0 = 0; e0 < cnt; e0 += 8) {
+    float z[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = buf[(e0 + j) * 64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (e0 + j < cnt && z[j] > t) {
+        buf[w * 64] = z[j];
+        ++w;
+      }
+    }
+  }
+  cnt = w;
+}
+
 template <class C, int NORM, bool CAP>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_kernel(FwdArgs a) {
   using SC = SparseCfg<C>;
@@ -703,6 +758,58 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   int cnt = 0;                // this lane's candidates
   bool ovf = !row_ok;         // row left to the extra passes (or no row at all)
   bool settled = false;       // floor has reached the exact threshold of the keys seen once
+
+  // The kTop largest lane-block maxima of z this lane has seen, descending.
+  // Each is the z of one key, so the threshold of the row's 2 kTop such
+  // values (both lanes) bounds tau from below -- and tightly, since the
+  // support consists mostly of block maxima.
+  constexpr int kTop = 8;
+  float top[kTop];
+#pragma unroll
+  for (int i = 0; i < kTop; ++i) top[i] = -INFINITY;
+  bool dirty = false;  // the list changed since the floor last used it
+  auto push_top = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kTop; ++i) {  // compare-exchange chain keeps the list sorted
+      const float hi = fmaxf(top[i], v);
+      v = fminf(top[i], v);
+      top[i] = hi;
+    }
+  };
+  // Threshold of the row's 2 kTop listed values (a lower bound when the
+  // steps do not settle).  Wave-uniform: partner exchanges.  Both lanes of a
+  // row order the values alike, so they compute the same floor.
+  auto top_floor = [&]() __attribute__((always_inline)) -> double {
+    float u[2 * kTop];
+#pragma unroll
+    for (int i = 0; i < kTop; ++i) {
+      const float o = partner(top[i]);
+      u[i] = g == 0 ? top[i] : o;
+      u[kTop + i] = g == 0 ? o : top[i];
+    }
+    const double mref = (double)fmaxf(u[0], u[kTop]);
+    double t = mref - 1.0;
+    for (int it = 0; it < 2 * kTop + 2; ++it) {
+      double c = 0.0, s1 = 0.0, s2 = 0.0;
+      float mn = INFINITY;
+#pragma unroll
+      for (int i = 0; i < 2 * kTop; ++i) {
+        if ((double)u[i] > t) {
+          const double y = (double)u[i] - mref;
+          c += 1.0;
+          s1 += y;
+          s2 += y * y;
+          mn = fminf(mn, u[i]);
+        }
+      }
+      if (!(c > 0.0)) break;
+      bool ex;
+      const double tn = thr_step<NORM>(c, s1, s2, mn, mref, t, ex);
+      if (ex) return tn;
+      t = fmax(t, tn);
+    }
+    return t;
+  };
 
   // Raises the floors until every row has room for a full block in both of
   // its lanes or its floor is the exact threshold of the keys seen so far
@@ -777,6 +884,13 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       }
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
+        if (bz[kb] > top[kTop - 1]) {
+          push_top(bz[kb]);
+          dirty = true;
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
         if (__any(bz[kb] > floor_f && !ovf)) {
           float z[16];
           int na = 0;
@@ -785,13 +899,28 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             z[r] = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
             na += z[r] > floor_f ? 1 : 0;
           }
-          // refloor when a lane cannot take the block, and, until the floor
-          // has once been exact, already when a lane lacks room for a full block
-          if (__any(!ovf && (cnt + na > SCAP || (!settled && cnt + 16 > SCAP)))) {
-            refloor();
+          if (__any(!ovf && cnt + na > SCAP)) {
+            // a lane cannot take the block: raise the floors from the lists
+            // of block maxima and drop what fell below them ...
+            if (__any(dirty)) {
+              const double tf = top_floor();
+              if (!ovf && tf > floor_) {
+                floor_ = tf;
+                floor_f = float_floor(floor_);
+              }
+              dirty = false;
+            }
+            compact_buf<SCAP>(buf, cnt, floor_f);
             na = 0;
 #pragma unroll
             for (int r = 0; r < 16; ++r) na += z[r] > floor_f ? 1 : 0;
+            // ... and, if that is not enough, step the floors on the buffers
+            if (__any(!ovf && cnt + na > SCAP)) {
+              refloor();
+              na = 0;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) na += z[r] > floor_f ? 1 : 0;
+            }
           }
           // a row whose lanes cannot take the block goes to the extra passes
           const int full = (!ovf && cnt + na > SCAP) ? 1 : 0;
