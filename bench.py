@@ -6,16 +6,23 @@ four normalizers (softmax, softmax1, sparsemax, 1.5-entmax) on the same
 synthetic inputs, already resident in HBM.  The metric is credited TFLOP/s:
 4 * head_dim FLOPs per unmasked (query, key) pair, the same for every
 normalizer (recomputed score passes of the sparse normalizers are not
-credited).  With --decode the paged-decode workload (64 sequences of
-1024..32768 keys, 16-token pages) is timed as well and reported in GB/s.
+credited).  `value` is the whole step (4 launches) over the wall clock of the
+timed steps.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode]
+Also reported (not part of `value`): per-launch medians over the timed steps
+(HIP events on the launch stream), the roofline of the slowest kernel, the
+Qwen3-1.7B-shaped prefill at three score scales (mean support size per scale),
+the Gemma-2-9B-shaped local layer, the paged-decode workload in GB/s (skip
+with --no-decode) and the fp64 CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
+       [--no-extra] [--no-cpu-baseline]
 Prints one JSON line.
 """
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import platform
 import sys
@@ -26,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", "prefill.hip")
 
 
 def credited_pairs(cfg):
@@ -60,6 +69,43 @@ def decode_bytes(x, cfg, seq_lens, norm, support=None):
     return k + v + q + q + table + cfg.B * 4
 
 
+def median_us(pairs):
+    ts = sorted(a.elapsed_time(b) for a, b in pairs)
+    return ts[len(ts) // 2] * 1e3
+
+
+def time_launches(f, reps, warmup):
+    """Median launch time (us) with HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return median_us(evs)
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the prefill source changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("prefill_src_sha256") != src or kernel_key not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel_key]
+    return int(k["read_bytes"] + k["write_bytes"])
+
+
 def cpu_baseline(cfg, budget_s=15.0):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -90,12 +136,71 @@ def cpu_baseline(cfg, budget_s=15.0):
                       f"(fp64 NumPy oracle, one row per call), {dt:.1f} s on {platform.processor() or 'host'}"}
 
 
+def extra_prefill(apn, W, dev, reps=10):
+    """Qwen3-1.7B-shaped sweep over the score scale, and the Gemma-2-9B-shaped
+    local layer: median launch time, credited TFLOP/s, mean support size."""
+    import torch
+    res = {}
+    for cfg in (W.qwen(0.5), W.qwen(1.0), W.qwen(2.0), W.GEMMA):
+        q, k, v = [x.to(dev) for x in W.make_prefill(cfg)]
+        out = torch.empty_like(q)
+        st = torch.empty(*q.shape[:3], 2, dtype=torch.float32, device=dev)
+        flops = 4 * cfg.D * credited_pairs(cfg)
+        per = {}
+        for n in cfg.normalizers:
+            f = lambda: apn.attn_fwd(q, k, v, out, st, normalizer=n, causal=cfg.causal,
+                                     window=cfg.window, softcap=cfg.softcap, scaling=cfg.scaling)
+            us = time_launches(f, reps, 2)
+            per[n] = {"us": round(us, 1), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                      "pct_bf16_peak": round(100 * flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+            if n in ("sparsemax", "entmax15"):
+                per[n]["mean_support"] = round(float(st[..., 1].mean()), 2)
+        res[cfg.name] = {"B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "L": cfg.Lq, "head_dim": cfg.D,
+                         "window": cfg.window, "softcap": cfg.softcap,
+                         "credited_flop_per_launch": flops, "per_normalizer": per}
+        del q, k, v, out, st
+        torch.cuda.empty_cache()
+    return res
+
+
+def decode_bench(apn, W, dev, reps):
+    import torch
+    dcfg = W.DECODE
+    x = W.make_paged(dcfg, device=dev)
+    lens = x.seq_lens.cpu().tolist()
+    paged = {"block_table": x.block_table, "seq_lens": x.seq_lens,
+             "block_size": x.block_size, "max_blocks": x.max_blocks}
+    dout = torch.empty_like(x.q)
+    dst = torch.empty(*x.q.shape[:3], 2, dtype=torch.float32, device=dev)
+    dres = {}
+    for n in dcfg.normalizers:
+        ws_n = apn.attn_fwd_workspace_bytes(x.q, x.k_cache, x.v_cache, normalizer=n,
+                                            causal=True, scaling=dcfg.scaling, paged=paged)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+        f = lambda: apn.attn_fwd(x.q, x.k_cache, x.v_cache, dout, dst, normalizer=n,
+                                 causal=True, scaling=dcfg.scaling, paged=paged, workspace=ws)
+        us = time_launches(f, reps, 3)
+        nbytes = decode_bytes(x, dcfg, lens, n, dst[..., 1].cpu())
+        dres[n] = {"us": round(us, 1), "bytes": nbytes,
+                   "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                   "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del ws
+    dom = max(dres, key=lambda n: dres[n]["us"])
+    return {"workload": dcfg.name, "B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv,
+            "head_dim": dcfg.D, "block_size": dcfg.block_size, "live_keys": int(sum(lens)),
+            "per_normalizer": dres,
+            "roofline": {"kernel": f"paged decode {dom}", "bound": "hbm",
+                         "achieved": dres[dom]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": dres[dom]["frac_hbm_peak"]}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
@@ -143,12 +248,12 @@ def main():
             evs[n].append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_norm_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in norms}
+    per_norm_us = {n: median_us(evs[n]) for n in norms}
     ms_per_step = wall * 1e3 / args.steps
     value = flops_per_launch * len(norms) / (ms_per_step * 1e-3) / 1e12
 
-    dom = max(norms, key=lambda n: per_norm_ms[n])
-    achieved = flops_per_launch / (per_norm_ms[dom] * 1e-3) / 1e12
+    dom = max(norms, key=lambda n: per_norm_us[n])
+    achieved = flops_per_launch / (per_norm_us[dom] * 1e-6) / 1e12
     result = {
         "metric": "attention fwd TFLOP/s per normalizer + % bf16 MFMA peak; decode HBM GB/s",
         "value": round(value, 2),
@@ -166,14 +271,15 @@ def main():
                    "head_dim": cfg.D, "causal": cfg.causal, "scaling": cfg.scaling,
                    "normalizers": norms, "credited_pairs": pairs,
                    "credited_flop_per_launch": flops_per_launch, "parallelism": "single GPU"},
-        "per_normalizer": {n: {"us": round(per_norm_ms[n] * 1e3, 1),
-                               "TFLOP/s": round(flops_per_launch / (per_norm_ms[n] * 1e-3) / 1e12, 1),
+        "per_normalizer": {n: {"us": round(per_norm_us[n], 1),
+                               "TFLOP/s": round(flops_per_launch / (per_norm_us[n] * 1e-6) / 1e12, 1),
                                "pct_bf16_peak": round(100 * flops_per_launch /
-                                                      (per_norm_ms[n] * 1e-3) / 1e12 /
+                                                      (per_norm_us[n] * 1e-6) / 1e12 /
                                                       PEAK_BF16_TFLOPS, 2)} for n in norms},
         "roofline": {"kernel": f"prefill {dom}", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(f"{cfg.name}:{dom}")},
     }
 
     if args.copy_calibration_mib:
@@ -186,41 +292,12 @@ def main():
         result["copy_calibration_bytes"] = n * 4
         del src, dst
 
-    if args.decode:
-        dcfg = W.DECODE
-        x = W.make_paged(dcfg, device=dev)
-        lens = x.seq_lens.cpu().tolist()
-        paged = {"block_table": x.block_table, "seq_lens": x.seq_lens,
-                 "block_size": x.block_size, "max_blocks": x.max_blocks}
-        dout = torch.empty_like(x.q)
-        dst = torch.empty(*x.q.shape[:3], 2, dtype=torch.float32, device=dev)
-        dres = {}
-        for n in dcfg.normalizers:
-            ws_n = apn.attn_fwd_workspace_bytes(x.q, x.k_cache, x.v_cache, normalizer=n,
-                                                causal=True, scaling=dcfg.scaling, paged=paged)
-            ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-            f = lambda: apn.attn_fwd(x.q, x.k_cache, x.v_cache, dout, dst, normalizer=n,
-                                     causal=True, scaling=dcfg.scaling, paged=paged, workspace=ws)
-            for _ in range(2):
-                f()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(max(3, args.steps)):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                f()
-                e1.record()
-                ts.append((e0, e1))
-            torch.cuda.synchronize()
-            ms = sorted(a.elapsed_time(b) for a, b in ts)[len(ts) // 2]
-            nbytes = decode_bytes(x, dcfg, lens, n, dst[..., 1].cpu())
-            dres[n] = {"us": round(ms * 1e3, 1), "bytes": nbytes,
-                       "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                       "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        result["decode"] = {"workload": dcfg.name, "B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv,
-                            "head_dim": dcfg.D, "block_size": dcfg.block_size,
-                            "live_keys": int(sum(lens)), "per_normalizer": dres}
+    del q, k, v, out, stats
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        result["prefill_workloads"] = extra_prefill(apn, W, dev)
+    if not args.no_decode:
+        result["decode"] = decode_bench(apn, W, dev, max(3, args.steps))
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)
