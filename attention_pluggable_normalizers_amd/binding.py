@@ -43,7 +43,7 @@ class _Paged(ctypes.Structure):
 class _Params(ctypes.Structure):
     _fields_ = [("normalizer", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
-                ("scaling", ctypes.c_float)]
+                ("scaling", ctypes.c_float), ("sinks", ctypes.c_void_p)]
 
 
 _lib = None
@@ -102,13 +102,21 @@ def _desc(t):
     return d
 
 
-def _params(normalizer, causal, window, softcap, scaling, head_dim):
+def _params(normalizer, causal, window, softcap, scaling, head_dim, sinks=None, num_heads=None):
     p = _Params()
     p.normalizer = NORMALIZER_IDS.get(normalizer, -1) if isinstance(normalizer, str) else int(normalizer)
     p.causal = 1 if causal else 0
     p.window = int(window)
     p.softcap = float(softcap)
     p.scaling = float(1.0 / math.sqrt(head_dim) if scaling is None else scaling)
+    if sinks is not None:
+        # the library reads Hq float32 values from this device address
+        if (sinks.dtype != torch.float32 or sinks.dim() != 1 or sinks.numel() != num_heads
+                or not sinks.is_contiguous() or sinks.device.type != "cuda"):
+            raise ValueError("sinks must be a contiguous float32 device tensor of shape [Hq]")
+        p.sinks = sinks.data_ptr()
+    else:
+        p.sinks = None
     return p
 
 
@@ -143,13 +151,15 @@ def attn_fwd_workspace_bytes(q, k, v, *, normalizer, causal=False, window=0, sof
 
 
 def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, window=0,
-             softcap=0.0, scaling=None, paged=None, workspace=None, stream=None):
+             softcap=0.0, scaling=None, paged=None, workspace=None, stream=None, sinks=None):
     """Enqueue the forward on ``stream`` (default: torch's current stream).
 
     q [B,Hq,Lq,D]; k, v [B,Hkv,Lk,D], or paged caches [NB,bs,Hkv,D] with
     ``paged = {"block_table", "seq_lens", "block_size", "max_blocks"}``.
     ``out`` (allocated like q when None) and ``row_stats`` (float32
     [B,Hq,Lq,2] or None) receive the results; returns ``(out, row_stats)``.
+    ``sinks`` (softmax1 only): float32 device tensor [Hq] of learned sink
+    logits, the virtual key's logit per query head (default 0).
     """
     lib = load_library()
     if out is None:
@@ -158,7 +168,7 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
                                   or tuple(row_stats.shape) != (*q.shape[:3], 2)):
         raise ValueError("row_stats must be a contiguous float32 tensor [B, Hq, Lq, 2]")
     pd = _paged_desc(paged)
-    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1])
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
     if workspace is None:
         nbytes = attn_fwd_workspace_bytes(q, k, v, normalizer=normalizer, causal=causal,
                                           window=window, softcap=softcap, scaling=scaling,
@@ -179,7 +189,7 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
 
 def custom_attention(module, query, key, value, attention_mask, *, normalizer, dropout=0.0,
                      scaling=None, is_causal=True, sliding_window=0, softcap=0.0,
-                     output_attentions=False, **kwargs):
+                     output_attentions=False, sinks=None, **kwargs):
     """The custom-attention signature of the transformers attention interface.
 
     ("attention interface", "custom attention registration": the function
@@ -188,6 +198,7 @@ def custom_attention(module, query, key, value, attention_mask, *, normalizer, d
     backend must support".)  query [B,Hq,L,D], key/value [B,Hkv,Lk,D] (GQA
     handled natively).  Only structured masks are supported, so a dense
     ``attention_mask`` is rejected, as are dropout and returned weights.
+    ``sinks`` (softmax1): per-head learned sink logits, float32 [Hq].
     Returns ``(out [B, L, Hq, D], None)``.
     """
     if attention_mask is not None:
@@ -197,5 +208,6 @@ def custom_attention(module, query, key, value, attention_mask, *, normalizer, d
     if output_attentions:
         raise AttnError(ATTN_E_UNSUPPORTED, "attention weights are never materialized")
     out, _ = attn_fwd(query, key, value, normalizer=normalizer, causal=is_causal,
-                      window=sliding_window or 0, softcap=softcap or 0.0, scaling=scaling)
+                      window=sliding_window or 0, softcap=softcap or 0.0, scaling=scaling,
+                      sinks=sinks)
     return out.transpose(1, 2).contiguous(), None

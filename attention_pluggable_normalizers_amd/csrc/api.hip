@@ -65,6 +65,8 @@ int validate(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   if (!(p->softcap >= 0.f) || !isfinite(p->softcap))
     return fail(ATTN_E_INVALID, "softcap must be finite and >= 0");
   if (!isfinite(p->scaling)) return fail(ATTN_E_INVALID, "scaling must be finite");
+  if (p->sinks && p->normalizer != ATTN_SOFTMAX1)
+    return fail(ATTN_E_INVALID, "sink logits apply to softmax1 only");
 
   const int64_t B = q->shape[0], Hq = q->shape[1], Lq = q->shape[2], D = q->shape[3];
   int64_t Hkv, Lk;
@@ -121,6 +123,7 @@ int validate(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   a->Lq = (int)Lq; a->Lk = (int)Lk; a->D = (int)D;
   a->norm = p->normalizer; a->causal = p->causal; a->window = p->window;
   a->softcap = p->softcap; a->scaling = p->scaling;
+  a->sinks = p->sinks;
   return ATTN_OK;
 }
 

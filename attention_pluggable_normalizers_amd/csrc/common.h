@@ -32,6 +32,7 @@ struct FwdArgs {
   int num_blocks;  // pages in each paged cache (page indices are clamped to it)
   int norm, causal, window;
   float softcap, scaling;
+  const float* sinks;  // softmax1: per query head logit of the virtual key (NULL = 0)
 };
 
 typedef __bf16 bf16_t;

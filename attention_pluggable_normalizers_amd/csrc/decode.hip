@@ -758,7 +758,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
   }
   float M = red[0];
   __syncthreads();
-  if (NORM == ATTN_SOFTMAX1) M = fmaxf(M, 0.f);
+  // softmax1: the virtual key at logit b (0, or the head's learned sink)
+  const float sink2 = (NORM == ATTN_SOFTMAX1 && a.sinks) ? a.sinks[qh] * kLog2e : 0.f;
+  if (NORM == ATTN_SOFTMAX1) M = fmaxf(M, sink2);
   const float mref = M == -INFINITY ? 0.f : M;
   float l = 0.f;
   for (int s = tid; s < ns; s += 256) {
@@ -772,7 +774,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
     __syncthreads();
   }
   float L = red[0];
-  if (NORM == ATTN_SOFTMAX1) L += __builtin_amdgcn_exp2f(-mref);  // the "+1" at logit 0
+  if (NORM == ATTN_SOFTMAX1) L += __builtin_amdgcn_exp2f(sink2 - mref);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   // weighted sum of the acc chunks
   const int g = tid / CH, c = tid - g * CH;

@@ -99,10 +99,12 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   T* orow = (T*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)i * a.o_sl;
   float* srow = a.stats ? a.stats + row * 2 : nullptr;
 
+  // softmax1: logit of the virtual key (0, or the head's learned sink)
+  const float sink = (NORM == ATTN_SOFTMAX1 && a.sinks) ? a.sinks[h] : 0.f;
   if (hi <= lo) {
     for (int d = lane; d < D; d += 64) orow[d] = from_f32<T>(0.f);
     if (srow && lane == 0) {
-      srow[0] = NORM == ATTN_SOFTMAX ? -INFINITY : (NORM == ATTN_SOFTMAX1 ? 0.f : INFINITY);
+      srow[0] = NORM == ATTN_SOFTMAX ? -INFINITY : (NORM == ATTN_SOFTMAX1 ? sink : INFINITY);
       srow[1] = NORM == ATTN_SOFTMAX1 ? 1.f : 0.f;
     }
     return;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   float acc[kMaxD / 64];
 #pragma unroll
   for (int c = 0; c < kMaxD / 64; ++c) acc[c] = 0.f;
-  const float mref = (NORM == ATTN_SOFTMAX1) ? fmaxf(m, 0.f) : m;
+  const float mref = (NORM == ATTN_SOFTMAX1) ? fmaxf(m, sink) : m;
   float lsum = 0.f;
   for (int base = lo; base < hi; base += 64) {
     const int j = base + lane;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   float st0, st1;
   if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1) {
     float l = wave_sum(lsum);
-    if (NORM == ATTN_SOFTMAX1) l += expf(-mref);
+    if (NORM == ATTN_SOFTMAX1) l += expf(sink - mref);
     inv = 1.f / l;
     st0 = mref;
     st1 = l;

@@ -372,9 +372,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
   // log2-domain reference max (accumulators are relative to it) and true max
-  float m_use = (NORM == ATTN_SOFTMAX1) ? 0.f : -INFINITY;
+  // softmax1: the virtual key's logit b (0, or the head's learned sink) is
+  // the initial max, and its weight exp(b - m) = 1 the initial sum
+  const float sink2 = (NORM == ATTN_SOFTMAX1 && a.sinks) ? a.sinks[h] * kLog2e : 0.f;
+  float m_use = (NORM == ATTN_SOFTMAX1) ? sink2 : -INFINITY;
   float m_true = m_use;
-  float lsum = (NORM == ATTN_SOFTMAX1 && g == 0) ? 1.f : 0.f;  // the softmax1 "+1" at logit 0
+  float lsum = (NORM == ATTN_SOFTMAX1 && g == 0) ? 1.f : 0.f;
   const float c2 = a.scaling * kLog2e;
   const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
   const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;

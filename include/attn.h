@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum attn_status {
@@ -104,13 +104,23 @@ typedef struct attn_paged_kv {
  *   softcap : 0 = none; else score <- softcap * tanh(score / softcap),
  *             applied after scaling and before the mask ("Attention
  *             variants", parameter table: logit_softcap).  Must be >= 0.
- *   scaling : multiplies Q K^T; must be finite.                           */
+ *   scaling : multiplies Q K^T; must be finite.
+ *   sinks   : NULL, or (softmax1 only) device float32 [Hq]: per query head
+ *             h the logit of softmax1's virtual key (value 0) in place of 0,
+ *             i.e. learned attention sinks, one more per-head term in the
+ *             softmax's denominator ("Attention variants: what to open up,
+ *             and how far", "What cannot be drawn today"):
+ *             w_j = exp(s_j) / (exp(sinks[h]) + sum_k exp(s_k)).  The logit
+ *             is used as given (no scaling, no softcap); values must be
+ *             finite.  Any other normalizer with sinks != NULL is
+ *             ATTN_E_INVALID.                                              */
 typedef struct attn_params {
   int32_t normalizer;  /* attn_normalizer */
   int32_t causal;      /* 0 or 1 */
   int32_t window;      /* >= 0 */
   float softcap;
   float scaling;
+  const float* sinks;  /* NULL or device float32 [Hq] (softmax1) */
 } attn_params;
 
 /* attn_fwd -- enqueue the forward on `stream` (a hipStream_t; NULL = the
@@ -126,10 +136,11 @@ typedef struct attn_params {
  *               no visible key get zeros).
  *   row_stats : NULL, or device float32 [B, Hq, Lq, 2], contiguous:
  *               softmax / softmax1 -> (m, l): the weights are exp(s - m) / l
- *               (softmax1: m = max(0, max s), l includes exp(-m));
+ *               (softmax1: m = max(b, max s), l includes exp(b - m), with
+ *               b = 0 or the head's sink logit);
  *               sparsemax / entmax15 -> (tau, k): threshold (in the s/2
  *               domain for entmax15) and support size, as a float.
- *               Rows with no visible key: (-inf, 0), (0, 1), (+inf, 0).
+ *               Rows with no visible key: (-inf, 0), (b, 1), (+inf, 0).
  *   workspace : device scratch of at least attn_fwd_workspace_bytes(...)
  *               bytes (may be NULL when that size is 0); its contents on entry
  *               are ignored and on return are unspecified.  It must not be

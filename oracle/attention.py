@@ -49,11 +49,13 @@ def _check_params(normalizer, causal, window, softcap, scaling):
 
 def attention_forward(q, k, v, normalizer, causal=False, window=0, softcap=0.0,
                       scaling=None, seq_lens=None, rows=None, return_probs=False,
-                      row_block=512):
+                      row_block=512, sinks=None):
     """Reference forward for q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
 
     ``seq_lens`` (optional, length B) limits the live keys of each batch entry
     (the paged path uses it; alignment stays bottom-right against it).
+    ``sinks`` (optional, length Hq, softmax1 only): per query head, the logit
+    of the virtual key in place of 0 (learned attention sinks).
     ``rows`` (optional) restricts the computation to a list of
     ``(b, h, i)`` query rows; then the result arrays hold only those rows, in
     that order: out [R, D], stats [R, 2].
@@ -91,7 +93,8 @@ def attention_forward(q, k, v, normalizer, causal=False, window=0, softcap=0.0,
 
     def finish_row(b, h, srow, mrow):
         idx = np.nonzero(mrow)[0]
-        p, st0, st1 = normalize_row(normalizer, srow[idx])
+        p, st0, st1 = normalize_row(normalizer, srow[idx],
+                                    None if sinks is None else float(sinks[h]))
         o = p @ v[b, h // G, idx] if idx.size else np.zeros(D)
         return idx, p, o, (st0, st1)
 
@@ -154,7 +157,7 @@ def gather_paged_kv(cache, block_table, seq_len, b):
 
 def paged_attention_forward(q, k_cache, v_cache, block_table, seq_lens, normalizer,
                             causal=True, window=0, softcap=0.0, scaling=None,
-                            rows=None, return_probs=False):
+                            rows=None, return_probs=False, sinks=None):
     """Reference forward over a paged KV cache: gather, then attend.
 
     q [B,Hq,Lq,D]; k_cache/v_cache [NB, block_size, Hkv, D]; block_table
@@ -180,7 +183,7 @@ def paged_attention_forward(q, k_cache, v_cache, block_table, seq_lens, normaliz
             vb = gather_paged_kv(v_cache, block_table, seq_lens[b], b)[None]
             res = attention_forward(q[b:b + 1], kb, vb, normalizer, causal, window,
                                     softcap, scaling, rows=[(0, h, i) for _, h, i in items],
-                                    return_probs=return_probs)
+                                    return_probs=return_probs, sinks=sinks)
             for n_, (r, _, _) in enumerate(items):
                 out[r] = res[0][n_]
                 stats[r] = res[1][n_]
@@ -195,7 +198,7 @@ def paged_attention_forward(q, k_cache, v_cache, block_table, seq_lens, normaliz
         kb = gather_paged_kv(k_cache, block_table, seq_lens[b], b)[None]
         vb = gather_paged_kv(v_cache, block_table, seq_lens[b], b)[None]
         o, st = attention_forward(q[b:b + 1], kb, vb, normalizer, causal, window,
-                                  softcap, scaling)
+                                  softcap, scaling, sinks=sinks)
         out[b] = o[0]
         stats[b] = st[0]
     return out, stats

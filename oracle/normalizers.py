@@ -40,25 +40,33 @@ def softmax_row(s):
     return e / l, m, l
 
 
-def softmax1_row(s):
+def softmax1_row(s, sink=0.0):
     """softmax1 (Softmax-N with n = 1): ``exp(s_i) / (1 + sum_j exp(s_j))``.
 
     Source: "HF Attention Normalizers", "Supported Normalizers" (the formula)
     and "Important Limitations" (the online kernel treats the "+1" as a
     virtual key with logit 0 and value 0, and saves row max and denominator).
 
-    Stabilised with ``m = max(0, max_j s_j)``: both numerator and denominator
-    are multiplied by ``exp(-m)``, so ``l = exp(-m) + sum_j exp(s_j - m)``.
-    Masked keys are absent; the "+1" is not a key and always stays.
+    ``sink`` generalises the virtual key's logit from 0 to a learned per-head
+    value b ("Attention variants: what to open up, and how far", "What cannot
+    be drawn today": attention sinks add one learned per-head term to the
+    softmax's denominator): ``exp(s_i) / (exp(b) + sum_j exp(s_j))``.
+
+    Stabilised with ``m = max(b, max_j s_j)``: both numerator and denominator
+    are multiplied by ``exp(-m)``, so ``l = exp(b - m) + sum_j exp(s_j - m)``.
+    Masked keys are absent; the virtual key is not a key and always stays.
     Pinned by: the closed form evaluated directly, the appended zero-key /
-    zero-value identity through PyTorch fp64 SDPA, and 1/(n+1) on zero rows.
+    zero-value identity through PyTorch fp64 SDPA, 1/(n+1) on zero rows, and
+    (sink) plain softmax over the row extended by the sink logit, and the limit
+    b -> -inf equal to softmax.
     """
     s = np.asarray(s, dtype=np.float64)
+    b = float(sink)
     if s.size == 0:
-        return np.zeros(0), 0.0, 1.0
-    m = max(0.0, float(np.max(s)))
+        return np.zeros(0), b, 1.0
+    m = max(b, float(np.max(s)))
     e = np.exp(s - m)
-    l = math.exp(-m) + float(np.sum(e))
+    l = math.exp(b - m) + float(np.sum(e))
     return e / l, m, l
 
 
@@ -148,10 +156,15 @@ _ROW_FUNCS = {
 }
 
 
-def normalize_row(name, s):
-    """Dispatch by normalizer name (one of ``NORMALIZERS``)."""
+def normalize_row(name, s, sink=None):
+    """Dispatch by normalizer name (one of ``NORMALIZERS``); ``sink`` (a
+    learned sink logit) applies to softmax1 only."""
     try:
         fn = _ROW_FUNCS[name]
     except KeyError:
         raise ValueError(f"unknown normalizer {name!r}") from None
+    if sink is not None:
+        if name != "softmax1":
+            raise ValueError("a sink logit applies to softmax1 only")
+        return fn(s, sink)
     return fn(s)

@@ -26,9 +26,10 @@ def to_dev(*xs):
     return [x.to("cuda") for x in xs]
 
 
-def gpu_fwd(q, k, v, norm, causal, window, softcap, scaling, paged=None):
+def gpu_fwd(q, k, v, norm, causal, window, softcap, scaling, paged=None, sinks=None):
     """Run libattn on device copies of q, k, v; returns fp64 numpy out and stats."""
     qd, kd, vd = to_dev(q, k, v)
+    sd = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).to("cuda")
     stats = torch.full((*q.shape[:3], 2), float("nan"), dtype=torch.float32, device="cuda")
     pdev = None
     if paged is not None:
@@ -36,7 +37,8 @@ def gpu_fwd(q, k, v, norm, causal, window, softcap, scaling, paged=None):
         pdev["block_table"] = paged["block_table"].to("cuda")
         pdev["seq_lens"] = paged["seq_lens"].to("cuda")
     out, _ = apn.attn_fwd(qd, kd, vd, None, stats, normalizer=norm, causal=causal,
-                          window=window, softcap=softcap, scaling=scaling, paged=pdev)
+                          window=window, softcap=softcap, scaling=scaling, paged=pdev,
+                          sinks=sd)
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), stats.double().cpu().numpy()
 
@@ -86,16 +88,16 @@ def check_full(q, k, v, norm, causal=False, window=0, softcap=0.0, scaling=None,
 
 
 def check_rows(out_g, st_g, rows, q, k, v, norm, causal, window, softcap, scaling, paged=None,
-               where=""):
+               where="", sinks=None):
     """Parity on sampled rows of a large problem (out and stats)."""
     if paged is None:
         out_o, st_o, det = attention_forward(q, k, v, norm, causal, window, softcap, scaling,
-                                             rows=rows, return_probs=True)
+                                             rows=rows, return_probs=True, sinks=sinks)
     else:
         out_o, st_o, det = paged_attention_forward(q, k, v, paged["block_table"].cpu().numpy(),
                                                    paged["seq_lens"].cpu().numpy(), norm,
                                                    causal, window, softcap, scaling, rows=rows,
-                                                   return_probs=True)
+                                                   return_probs=True, sinks=sinks)
     worst = 0.0
     for r, (b, h, i) in enumerate(rows):
         e = float(np.abs(out_g[b, h, i] - out_o[r]).max())

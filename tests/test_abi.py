@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 1
+    assert apn.attn_abi_version() == 2
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -100,6 +100,9 @@ KV = (2, 2, 64, 64)
      "contiguous"),
     (lambda a: a["q"].__setattr__("data", 0), 1, "NULL"),
     (lambda a: a["q"].__setattr__("reserved", 3), 1, "reserved"),
+    (lambda a: a["p"].__setattr__("sinks", 0x4000), 1, "softmax1"),  # sinks with softmax
+    (lambda a: (a["p"].__setattr__("sinks", 0x4000), a["p"].__setattr__("normalizer", 3)), 1,
+     "softmax1"),
 ])
 def test_invalid_arguments_rejected(lib, mutate, code, needle):
     a = {"q": _t(Q), "k": _t(KV), "v": _t(KV), "p": _p(), "out": _t(Q)}

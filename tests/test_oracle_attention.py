@@ -269,3 +269,46 @@ def test_tiny_workload_runs():
         for causal, window in ((False, 0), (True, 4)):
             out, st = attention_forward(q, k, v, norm, causal, window, 0.0, 0.25)
             assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("causal,window,softcap", [(False, 0, 0.0), (True, 0, 0.0), (True, 4, 3.0)])
+def test_learned_sinks_are_sdpa_with_a_biased_zero_key(causal, window, softcap):
+    # a learned sink b_h is one extra key of value 0 whose logit is b_h for
+    # every query ("Attention variants: what to open up, and how far", "What
+    # cannot be drawn today"): SDPA with a zero key and an additive float mask
+    # that puts b_h on that key's column and -inf on masked keys
+    lq = lk = 10
+    q = _rand((1, 4, lq, 8), 14, 1.5)
+    k = _rand((1, 2, lk, 8), 15, 1.5)
+    v = _rand((1, 2, lk, 8), 16)
+    sinks = np.array([-1.5, 0.0, 0.7, 3.0])
+    out, stats = attention_forward(q, k, v, "softmax1", causal, window, softcap, 0.5, sinks=sinks)
+    allowed = allowed_mask(lq, lk, causal, window)
+    # scores with softcap applied, as the reference of the real keys
+    s = 0.5 * np.einsum("hid,hjd->hij", q[0], np.repeat(k[0], 2, axis=0))
+    if softcap:
+        s = softcap * np.tanh(s / softcap)
+    bias = np.where(allowed[None], s, -np.inf)                                  # [4, lq, lk]
+    bias = np.concatenate([np.broadcast_to(sinks[:, None, None], (4, lq, 1)), bias], axis=2)
+    v1 = np.concatenate([np.zeros((1, 2, 1, 8)), v], axis=2)
+    # scores come entirely from the float mask: zero queries and keys
+    t = lambda x: torch.tensor(x, dtype=torch.float64)
+    want = F.scaled_dot_product_attention(t(np.zeros((1, 4, lq, 8))), t(np.zeros((1, 2, lk + 1, 8))),
+                                          t(v1), attn_mask=t(bias[None]), enable_gqa=True).numpy()
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13)
+    # m = max(b, max s) per row
+    assert (stats[..., 0] >= sinks[None, :, None] - 1e-15).all()
+
+
+def test_learned_sink_limits():
+    q = _rand((1, 2, 6, 8), 17)
+    k = _rand((1, 1, 6, 8), 18)
+    v = _rand((1, 1, 6, 8), 19)
+    o_sm, _ = attention_forward(q, k, v, "softmax", True, 0, 0.0, 0.4)
+    o_far, _ = attention_forward(q, k, v, "softmax1", True, 0, 0.0, 0.4, sinks=[-800.0, -800.0])
+    np.testing.assert_allclose(o_far, o_sm, rtol=1e-13, atol=1e-15)
+    o_s1, st_s1 = attention_forward(q, k, v, "softmax1", True, 0, 0.0, 0.4)
+    o_z, st_z = attention_forward(q, k, v, "softmax1", True, 0, 0.0, 0.4, sinks=[0.0, 0.0])
+    assert np.array_equal(o_s1, o_z) and np.array_equal(st_s1, st_z)
+    with pytest.raises(ValueError):
+        attention_forward(q, k, v, "softmax", True, 0, 0.0, 0.4, sinks=[0.0, 0.0])

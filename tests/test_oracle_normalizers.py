@@ -254,3 +254,16 @@ def test_sparsemax_is_simplex_projection():
     for _ in range(2000):
         x = rng.dirichlet(np.ones(6) * 0.3)
         assert np.sum((x - z) ** 2) >= best - 1e-12
+
+
+@pytest.mark.parametrize("sink", [-3.0, 0.0, 1.25, 40.0])
+def test_softmax1_sink_is_softmax_of_the_extended_row(sink):
+    s = np.random.default_rng(5).normal(size=9) * 3.0
+    p, m, l = softmax1_row(s, sink)
+    e = np.exp(np.append(s, sink) - max(sink, s.max()))
+    np.testing.assert_allclose(p, (e / e.sum())[:-1], rtol=1e-14)
+    assert m == max(sink, s.max())
+    # literal closed form exp(s) / (exp(b) + sum exp(s)) where it cannot overflow
+    if sink < 30:
+        np.testing.assert_allclose(p, np.exp(s) / (math.exp(sink) + np.exp(s).sum()), rtol=1e-13)
+    assert softmax1_row(np.zeros(0), sink)[1:] == (sink, 1.0)
