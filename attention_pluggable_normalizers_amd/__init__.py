@@ -14,6 +14,7 @@ from .binding import (
     AttnError,
     attn_abi_version,
     attn_fwd,
+    attn_fwd_varlen,
     attn_fwd_workspace_bytes,
     attn_last_error_detail,
     attn_strerror,
@@ -31,6 +32,7 @@ __all__ = [
     "AttnError",
     "attn_abi_version",
     "attn_fwd",
+    "attn_fwd_varlen",
     "attn_fwd_workspace_bytes",
     "attn_last_error_detail",
     "attn_strerror",

@@ -40,6 +40,11 @@ class _Paged(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
 
 
+class _Varlen(ctypes.Structure):
+    _fields_ = [("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("num_seqs", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32)]
+
+
 class _Params(ctypes.Structure):
     _fields_ = [("normalizer", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
@@ -64,6 +69,10 @@ def load_library(path=None):
                              P(_Tensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                              ctypes.c_void_p]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_varlen.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Varlen), P(_Params),
+                                    P(_Tensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]
+    lib.attn_fwd_varlen.restype = ctypes.c_int
     lib.attn_fwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged),
                                              P(_Params), P(ctypes.c_size_t)]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_int
@@ -183,6 +192,49 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
                       ctypes.byref(_desc(out)),
                       row_stats.data_ptr() if row_stats is not None else None,
                       ws_ptr, ws_len, stream)
+    _check(st)
+    return out, row_stats
+
+
+def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None,
+                    row_stats=None, *, normalizer, causal=False, window=0, softcap=0.0,
+                    scaling=None, stream=None, sinks=None):
+    """Packed variable-length forward ("HF Attention Normalizers", "Packed
+    Variable-Length Attention").
+
+    query [total_q, Hq, D], key/value [total_k, Hkv, D]; cu_seqlens_q/k int32
+    device tensors [num_seqs + 1]; request r attends its own key range with
+    bottom-right causal alignment.  ``out`` [total_q, Hq, D] (allocated when
+    None) and ``row_stats`` (float32 [Hq, total_q, 2] or None) receive the
+    results; returns ``(out, row_stats)``.
+    """
+    lib = load_library()
+    if query.dim() != 3 or key.dim() != 3 or value.dim() != 3:
+        raise ValueError("packed query/key/value are [tokens, heads, head_dim]")
+    for t, name in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor [num_seqs + 1]")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty(query.shape, dtype=query.dtype, device=query.device)
+    if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+                                  or tuple(row_stats.shape) != (query.shape[1], query.shape[0], 2)):
+        raise ValueError("row_stats must be a contiguous float32 tensor [Hq, total_q, 2]")
+    view = lambda t: t.permute(1, 0, 2).unsqueeze(0)  # [1, heads, tokens, D], no copy
+    vl = _Varlen()
+    vl.cu_seqlens_q = cu_seqlens_q.data_ptr()
+    vl.cu_seqlens_k = cu_seqlens_k.data_ptr()
+    vl.num_seqs = cu_seqlens_q.numel() - 1
+    vl.max_seqlen_q = int(max_seqlen_q)
+    p = _params(normalizer, causal, window, softcap, scaling, query.shape[-1], sinks, query.shape[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device).cuda_stream
+    st = lib.attn_fwd_varlen(ctypes.byref(_desc(view(query))), ctypes.byref(_desc(view(key))),
+                             ctypes.byref(_desc(view(value))), ctypes.byref(vl), ctypes.byref(p),
+                             ctypes.byref(_desc(view(out))),
+                             row_stats.data_ptr() if row_stats is not None else None,
+                             None, 0, stream)
     _check(st)
     return out, row_stats
 

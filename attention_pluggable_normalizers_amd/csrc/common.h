@@ -33,7 +33,21 @@ struct FwdArgs {
   int norm, causal, window;
   float softcap, scaling;
   const float* sinks;  // softmax1: per query head logit of the virtual key (NULL = 0)
+  // packed variable-length batch (cu_q != nullptr): B = number of requests,
+  // Lq / Lk = packed token counts, max_q bounds every request's query count
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int max_q;
 };
+
+// Query/key token ranges of packed request r, clamped into the packed arrays.
+__device__ __forceinline__ void varlen_ranges(const FwdArgs& a, int r, int& q0, int& q1, int& k0,
+                                              int& k1) {
+  q0 = min(max(a.cu_q[r], 0), a.Lq);
+  q1 = min(max(a.cu_q[r + 1], q0), a.Lq);
+  k0 = min(max(a.cu_k[r], 0), a.Lk);
+  k1 = min(max(a.cu_k[r + 1], k0), a.Lk);
+}
 
 typedef __bf16 bf16_t;
 

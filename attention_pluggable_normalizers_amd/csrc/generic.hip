@@ -35,11 +35,16 @@ struct RowCtx {
   const T* kbase;      // contiguous: K of (b, kv head); paged: cache base + head offset
   const T* vbase;
   const int32_t* table;  // paged: this sequence's block-table row
-  __device__ RowCtx(const FwdArgs& a_, int b, int kvh) : a(a_) {
+  // key0: first key token of a packed request (0 otherwise)
+  __device__ RowCtx(const FwdArgs& a_, int b, int kvh, int key0) : a(a_) {
     if (a.paged) {
       kbase = (const T*)a.k + (int64_t)kvh * a.k_sh;
       vbase = (const T*)a.v + (int64_t)kvh * a.v_sh;
       table = a.block_table + (int64_t)b * a.max_blocks;
+    } else if (a.cu_q) {
+      kbase = (const T*)a.k + (int64_t)key0 * a.k_sl + (int64_t)kvh * a.k_sh;
+      vbase = (const T*)a.v + (int64_t)key0 * a.v_sl + (int64_t)kvh * a.v_sh;
+      table = nullptr;
     } else {
       kbase = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
       vbase = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
@@ -67,25 +72,48 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   __shared__ float qs[kMaxD];
   __shared__ float ps[64];
 
-  const int64_t row = blockIdx.x;  // ((b * Hq) + h) * Lq + i
-  const int i = (int)(row % a.Lq);
-  const int64_t bh = row / a.Lq;
-  const int h = (int)(bh % a.Hq);
-  const int b = (int)(bh / a.Hq);
-  const int kvh = h / a.G;
+  const int64_t row = blockIdx.x;  // ((b * Hq) + h) * Lq + i; packed: h * Lq + token
   const int lane = threadIdx.x;
   const int D = a.D;
+  int b, h, i, tok, nq, live, key0 = 0;
+  if (!a.cu_q) {
+    i = (int)(row % a.Lq);
+    const int64_t bh = row / a.Lq;
+    h = (int)(bh % a.Hq);
+    b = (int)(bh / a.Hq);
+    tok = i;
+    nq = a.Lq;
+    live = a.paged ? paged_live(a, b) : a.Lk;
+  } else {
+    // packed: the request holding this query token (binary search)
+    tok = (int)(row % a.Lq);
+    h = (int)(row / a.Lq);
+    int lo_r = 0, hi_r = a.B;  // last r with cu_q[r] <= tok
+    while (hi_r - lo_r > 1) {
+      const int mid = (lo_r + hi_r) >> 1;
+      if (a.cu_q[mid] <= tok) lo_r = mid;
+      else hi_r = mid;
+    }
+    b = lo_r;
+    int q0, q1, k0, k1;
+    varlen_ranges(a, b, q0, q1, k0, k1);
+    if (tok < q0 || tok >= q1) return;  // token outside every request: left unwritten
+    i = tok - q0;
+    nq = q1 - q0;
+    live = k1 - k0;
+    key0 = k0;
+  }
+  const int kvh = h / a.G;
+  const int64_t bq = a.cu_q ? 0 : b;  // batch index of the q / out / stats arrays
 
-  const T* qrow = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)i * a.q_sl;
+  const T* qrow = (const T*)a.q + bq * a.q_sb + (int64_t)h * a.q_sh + (int64_t)tok * a.q_sl;
   for (int d = lane; d < D; d += 64) qs[d] = to_f32(qrow[d]);
   __syncthreads();
 
-  int live = a.Lk;
-  if (a.paged) live = paged_live(a, b);
   int lo, hi;
-  key_range(i, a.Lq, live, a.causal, a.window, lo, hi);
+  key_range(i, nq, live, a.causal, a.window, lo, hi);
 
-  RowCtx<T> ctx(a, b, kvh);
+  RowCtx<T> ctx(a, b, kvh, key0);
   const bool entmax = (NORM == ATTN_ENTMAX15);
   auto zval = [&](int j) -> float {
     const T* kp = ctx.key(j);
@@ -96,7 +124,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
     return entmax ? 0.5f * s : s;
   };
 
-  T* orow = (T*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)i * a.o_sl;
+  T* orow = (T*)a.out + bq * a.o_sb + (int64_t)h * a.o_sh + (int64_t)tok * a.o_sl;
   float* srow = a.stats ? a.stats + row * 2 : nullptr;
 
   // softmax1: logit of the virtual key (0, or the head's learned sink)
@@ -226,7 +254,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
 
 template <typename T>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  const int64_t rows = (int64_t)(a.cu_q ? 1 : a.B) * a.Hq * a.Lq;
   dim3 grid((unsigned)rows), block(64);
   switch (a.norm) {
     case ATTN_SOFTMAX:

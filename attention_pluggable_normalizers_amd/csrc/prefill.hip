@@ -108,6 +108,39 @@ __device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
   qb = nqb - 1 - (id - bh * nqb);
 }
 
+// Query-row extent of the grid: the longest packed request, or Lq.
+__device__ __host__ __forceinline__ int q_extent(const FwdArgs& a) { return a.cu_q ? a.max_q : a.Lq; }
+
+// The sequence of one workgroup: batch entry b, or packed request b.
+struct SeqSpan {
+  int Lq, Lk;                            // its query and key counts
+  int64_t q_off, k_off, v_off, o_off;    // element offsets of its first query / key
+  int64_t st_row;                        // row_stats row of its query 0 for head h
+};
+__device__ __forceinline__ SeqSpan seq_span(const FwdArgs& a, int b, int h) {
+  SeqSpan s;
+  if (!a.cu_q) {
+    s.Lq = a.Lq;
+    s.Lk = a.Lk;
+    s.q_off = (int64_t)b * a.q_sb;
+    s.k_off = (int64_t)b * a.k_sb;
+    s.v_off = (int64_t)b * a.v_sb;
+    s.o_off = (int64_t)b * a.o_sb;
+    s.st_row = ((int64_t)b * a.Hq + h) * a.Lq;
+  } else {
+    int q0, q1, k0, k1;
+    varlen_ranges(a, b, q0, q1, k0, k1);
+    s.Lq = q1 - q0;
+    s.Lk = k1 - k0;
+    s.q_off = (int64_t)q0 * a.q_sl;
+    s.k_off = (int64_t)k0 * a.k_sl;
+    s.v_off = (int64_t)k0 * a.v_sl;
+    s.o_off = (int64_t)q0 * a.o_sl;
+    s.st_row = (int64_t)h * a.Lq + q0;
+  }
+  return s;
+}
+
 // Buffer resource over `bytes` bytes at `base`: raw buffer loads past the end
 // return zeros, which is how the ragged last key tile is read.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -324,16 +357,18 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int Lq = a.Lq, Lk = a.Lk;
-  const int nqb = (Lq + C::BM - 1) / C::BM;
+  const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   int bh, qb;
   block_coords(nqb, bh, qb);
   const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
   const int q0 = qb * C::BM;
+  const SeqSpan sp = seq_span(a, b, h);
+  if (q0 >= sp.Lq) return;  // packed request shorter than the longest one
+  const int Lq = sp.Lq, Lk = sp.Lk;
 
-  const bf16_t* qbase = (const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
-  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-  const bf16_t* vbase = (const bf16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+  const bf16_t* qbase = (const bf16_t*)a.q + sp.q_off + (int64_t)h * a.q_sh;
+  const bf16_t* kbase = (const bf16_t*)a.k + sp.k_off + (int64_t)kvh * a.k_sh;
+  const bf16_t* vbase = (const bf16_t*)a.v + sp.v_off + (int64_t)kvh * a.v_sh;
 
   // key tiles the workgroup visits
   const int qlast = min(q0 + C::BM, Lq) - 1;
@@ -501,7 +536,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const float ltot = pair_sum(lsum);
   if (row_ok) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
+    bf16_t* orow = (bf16_t*)a.out + sp.o_off + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
@@ -512,7 +547,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
       }
     }
     if (a.stats && g == 0) {
-      float* st = a.stats + (((int64_t)b * a.Hq + h) * Lq + myq) * 2;
+      float* st = a.stats + (sp.st_row + myq) * 2;
       const bool any_key = m_true != -INFINITY;
       st[0] = any_key ? m_true * (1.f / kLog2e) : -INFINITY;
       // denominator relative to the true max
@@ -713,16 +748,18 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int Lq = a.Lq, Lk = a.Lk;
-  const int nqb = (Lq + C::BM - 1) / C::BM;
+  const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   int bh, qb;
   block_coords(nqb, bh, qb);
   const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
   const int q0 = qb * C::BM;
+  const SeqSpan sp = seq_span(a, b, h);
+  if (q0 >= sp.Lq) return;  // packed request shorter than the longest one
+  const int Lq = sp.Lq, Lk = sp.Lk;
 
-  const bf16_t* qbase = (const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
-  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-  const bf16_t* vbase = (const bf16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+  const bf16_t* qbase = (const bf16_t*)a.q + sp.q_off + (int64_t)h * a.q_sh;
+  const bf16_t* kbase = (const bf16_t*)a.k + sp.k_off + (int64_t)kvh * a.k_sh;
+  const bf16_t* vbase = (const bf16_t*)a.v + sp.v_off + (int64_t)kvh * a.v_sh;
 
   const int qlast = min(q0 + C::BM, Lq) - 1;
   const RowBounds first = row_bounds(q0, Lq, Lk, a.causal, a.window);
@@ -1149,7 +1186,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   const float wtot = wsum + partner(wsum);
   if (row_ok) {
     const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
-    bf16_t* orow = (bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
+    bf16_t* orow = (bf16_t*)a.out + sp.o_off + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
@@ -1161,7 +1198,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       }
     }
     if (a.stats && g == 0) {
-      float* st = a.stats + (((int64_t)b * a.Hq + h) * Lq + myq) * 2;
+      float* st = a.stats + (sp.st_row + myq) * 2;
       st[0] = (float)tau;
       st[1] = (float)ksup;
     }
@@ -1170,7 +1207,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 
 template <class C, int NORM>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.Lq + C::BM - 1) / C::BM;
+  const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   dim3 grid((unsigned)(nqb * a.B * a.Hq)), block(C::NT);
   const bool cap = a.softcap > 0.f;
   if constexpr (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
@@ -1212,7 +1249,7 @@ bool prefill_mfma_supported(const FwdArgs& a) {
   // K/V slices are addressed through 32-bit buffer records
   if ((int64_t)a.Lk * a.k_sl * 2 >= ((int64_t)1 << 31) || (int64_t)a.Lk * a.v_sl * 2 >= ((int64_t)1 << 31))
     return false;
-  const int nqb_min = (a.Lq + 127) / 128;
+  const int nqb_min = (q_extent(a) + 127) / 128;
   return (int64_t)nqb_min * a.B * a.Hq <= (int64_t)INT32_MAX;
 }
 

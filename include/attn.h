@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum attn_status {
@@ -156,6 +156,37 @@ int attn_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
              const attn_paged_kv* paged, const attn_params* p,
              const attn_tensor* out, float* row_stats,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Packed variable-length batch ("HF Attention Normalizers", "Packed
+ * Variable-Length Attention": FlashAttention-style packed Q/K/V with
+ * cumulative sequence lengths, GQA, different Q/K lengths and per-request
+ * bottom-right causal alignment).  Request r owns query tokens
+ * [cu_seqlens_q[r], cu_seqlens_q[r+1]) and key tokens
+ * [cu_seqlens_k[r], cu_seqlens_k[r+1]); it attends like a batch entry of
+ * its own (causal / window aligned bottom-right against its key count).
+ * The arrays must start at 0 and be non-decreasing, with the last entries
+ * at most the packed token counts; values outside that range are clamped
+ * into it on the device.  max_seqlen_q must be >= every request's query
+ * count (rows of a longer request beyond it are not computed); query tokens
+ * outside every request are not written.                                   */
+typedef struct attn_varlen {
+  const int32_t* cu_seqlens_q;  /* device, int32 [num_seqs + 1] */
+  const int32_t* cu_seqlens_k;  /* device, int32 [num_seqs + 1] */
+  int32_t num_seqs;             /* >= 0 */
+  int32_t max_seqlen_q;         /* >= 0 */
+} attn_varlen;
+
+/* attn_fwd_varlen -- attn_fwd over a packed variable-length batch.
+ *   q, out : [1, Hq, total_q, D] (a packed [total_q, Hq, D] array is the
+ *            view with strides {., D, Hq*D, 1});
+ *   k, v   : [1, Hkv, total_k, D] likewise;
+ *   row_stats : NULL or device float32 [1, Hq, total_q, 2], contiguous.
+ * Parameters, dtypes, kernels and errors as attn_fwd (no paged cache; no
+ * workspace is needed: workspace may be NULL).                             */
+int attn_fwd_varlen(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                    const attn_varlen* varlen, const attn_params* p,
+                    const attn_tensor* out, float* row_stats,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* attn_fwd_workspace_bytes -- workspace size attn_fwd needs for these
  * arguments (host computation only; no device access).  Validates the same

@@ -19,7 +19,9 @@ What it computes (the forward the pages describe)::
 * the mask is causal and/or a sliding window ("attention interface",
   "flexattention patterns"; "tensorplay.nn.attention", create_mask example),
   plus the per-sequence length of a paged KV cache
-  ("HF Attention Normalizers", "Differentiable Paged Attention").
+  ("HF Attention Normalizers", "Differentiable Paged Attention"), or the
+  per-request ranges of a packed variable-length batch (same page, "Packed
+  Variable-Length Attention").
 
 Every floating-point step runs in float64.  Pins: see ``tests/test_oracle_*.py``.
 Parity status of each function is stated in its docstring; all are pinned.
@@ -34,7 +36,8 @@ from .normalizers import (
     entmax15_row,
     normalize_row,
 )
-from .attention import attention_forward, paged_attention_forward, gather_paged_kv
+from .attention import (attention_forward, paged_attention_forward, gather_paged_kv,
+                        varlen_attention_forward)
 
 __all__ = [
     "allowed_mask",
@@ -48,4 +51,5 @@ __all__ = [
     "attention_forward",
     "paged_attention_forward",
     "gather_paged_kv",
+    "varlen_attention_forward",
 ]

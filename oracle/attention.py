@@ -202,3 +202,37 @@ def paged_attention_forward(q, k_cache, v_cache, block_table, seq_lens, normaliz
         out[b] = o[0]
         stats[b] = st[0]
     return out, stats
+
+
+def varlen_attention_forward(q, k, v, cu_seqlens_q, cu_seqlens_k, normalizer, causal=False,
+                             window=0, softcap=0.0, scaling=None, sinks=None):
+    """Reference forward over a packed variable-length batch.
+
+    q [total_q, Hq, D], k/v [total_k, Hkv, D]; request r owns query tokens
+    cu_seqlens_q[r]..cu_seqlens_q[r+1] and key tokens cu_seqlens_k[r]..
+    cu_seqlens_k[r+1] and is attended as a batch entry of its own, causal and
+    window aligned bottom-right against its key count ("HF Attention
+    Normalizers", "Packed Variable-Length Attention").  Returns out
+    [total_q, Hq, D] and row_stats [Hq, total_q, 2]; query tokens outside every
+    request stay zero.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k)]
+    total_q, Hq, D = q.shape
+    out = np.zeros((total_q, Hq, D))
+    stats = np.zeros((Hq, total_q, 2))
+    for r in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[r], cq[r + 1], ck[r], ck[r + 1]
+        if q1 == q0:
+            continue
+        qr = np.transpose(q[q0:q1], (1, 0, 2))[None]
+        kr = np.transpose(k[k0:k1], (1, 0, 2))[None]
+        vr = np.transpose(v[k0:k1], (1, 0, 2))[None]
+        o, st = attention_forward(qr, kr, vr, normalizer, causal, window, softcap, scaling,
+                                  sinks=sinks)
+        out[q0:q1] = np.transpose(o[0], (1, 0, 2))
+        stats[:, q0:q1] = st[0]
+    return out, stats

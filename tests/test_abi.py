@@ -30,14 +30,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert names == sorted(["attn_fwd", "attn_fwd_workspace_bytes", "attn_strerror",
+    assert names == sorted(["attn_fwd", "attn_fwd_varlen", "attn_fwd_workspace_bytes", "attn_strerror",
                             "attn_last_error_detail", "attn_abi_version"])
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 2
+    assert apn.attn_abi_version() == 3
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -169,3 +169,24 @@ def test_python_wrapper_rejects_dense_mask_and_dropout():
         apn.custom_attention(None, q, q, q, None, normalizer="softmax", dropout=0.1)
     with pytest.raises(apn.AttnError):
         apn.custom_attention(None, q, q, q, None, normalizer="softmax", output_attentions=True)
+
+
+def test_varlen_validation(lib):
+    q = _t((1, 8, 100, 64))
+    kv = _t((1, 2, 120, 64))
+    vl = B._Varlen()
+    vl.cu_seqlens_q, vl.cu_seqlens_k, vl.num_seqs, vl.max_seqlen_q = 0x5000, 0x6000, 3, 50
+    call = lambda q_, kv_, v_: (lib.attn_fwd_varlen(ctypes.byref(q_), ctypes.byref(kv_),
+                                                    ctypes.byref(kv_), v_, ctypes.byref(_p()),
+                                                    ctypes.byref(q_), None, None, 0, None),
+                                apn.attn_last_error_detail())
+    r, d = call(q, kv, None)
+    assert r == 1 and "varlen" in d
+    r, d = call(_t((2, 8, 100, 64)), _t((2, 2, 120, 64)), ctypes.byref(vl))
+    assert r == 1 and "batch extent 1" in d
+    vl.num_seqs = -1
+    r, d = call(q, kv, ctypes.byref(vl))
+    assert r == 1 and "num_seqs" in d
+    vl.num_seqs, vl.cu_seqlens_k = 3, 0
+    r, d = call(q, kv, ctypes.byref(vl))
+    assert r == 1 and "NULL" in d

@@ -312,3 +312,34 @@ def test_learned_sink_limits():
     assert np.array_equal(o_s1, o_z) and np.array_equal(st_s1, st_z)
     with pytest.raises(ValueError):
         attention_forward(q, k, v, "softmax", True, 0, 0.0, 0.4, sinks=[0.0, 0.0])
+
+
+def test_varlen_equals_padded_batch_sdpa():
+    # packed requests with their own lengths (Lq <= Lk, bottom-right causal)
+    # against PyTorch SDPA on a zero-padded batch with an explicit mask
+    from oracle import varlen_attention_forward
+    lq = [3, 0, 7, 1, 5]
+    lk = [5, 2, 7, 4, 9]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    Hq, Hkv, D = 4, 2, 8
+    q = _rand((cq[-1], Hq, D), 21)
+    k = _rand((ck[-1], Hkv, D), 22)
+    v = _rand((ck[-1], Hkv, D), 23)
+    out, st = varlen_attention_forward(q, k, v, cq, ck, "softmax", True, 3, 0.0, 0.4)
+    B, Lq, Lk = len(lq), max(lq), max(lk)
+    qp = np.zeros((B, Hq, Lq, D)); kp = np.zeros((B, Hkv, Lk, D)); vp = np.zeros((B, Hkv, Lk, D))
+    mask = np.zeros((B, 1, Lq, Lk), bool)
+    for r in range(B):
+        qp[r, :, :lq[r]] = np.transpose(q[cq[r]:cq[r + 1]], (1, 0, 2))
+        kp[r, :, :lk[r]] = np.transpose(k[ck[r]:ck[r + 1]], (1, 0, 2))
+        vp[r, :, :lk[r]] = np.transpose(v[ck[r]:ck[r + 1]], (1, 0, 2))
+        for i in range(lq[r]):
+            for j in range(lk[r]):
+                qpos = i + lk[r] - lq[r]
+                mask[r, 0, i, j] = j <= qpos and qpos - j < 3
+    mask[..., 0] |= ~mask.any(-1)  # keep SDPA defined on padded rows (ignored)
+    want = _sdpa(qp, kp, vp, mask, 0.4)
+    for r in range(B):
+        got = np.transpose(out[cq[r]:cq[r + 1]], (1, 0, 2))
+        np.testing.assert_allclose(got, want[r, :, :lq[r]], rtol=1e-12, atol=1e-13)

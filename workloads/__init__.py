@@ -18,6 +18,8 @@ datasets are involved.
 from dataclasses import dataclass, field
 import math
 
+import itertools
+
 import torch
 
 NORMALIZERS = ("softmax", "softmax1", "sparsemax", "entmax15")
@@ -159,3 +161,34 @@ def make_paged(cfg, device="cpu", nan_tail=True):
     return PagedInputs(q, kc, vc, table.to(device), lens.to(device), bs, max_blocks,
                        extra={"pages": pages, "num_blocks": nb})
 
+
+
+@dataclass
+class Varlen:
+    """A packed variable-length batch: request r has q_lens[r] queries and
+    k_lens[r] keys (k_lens[r] >= q_lens[r] for a chunked-prefill shape)."""
+    name: str
+    q_lens: tuple
+    k_lens: tuple
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool
+    window: int
+    softcap: float
+    scaling: float
+    seed: int = 1000
+
+
+def make_varlen(cfg, device="cpu"):
+    """Packed q [total_q, Hq, D], k/v [total_k, Hkv, D] and int32
+    cu_seqlens_q / cu_seqlens_k [num_seqs + 1]."""
+    gen = torch.Generator(device=device).manual_seed(cfg.seed)
+    tq, tk = sum(cfg.q_lens), sum(cfg.k_lens)
+    q = _normal(gen, (tq, cfg.Hq, cfg.D), 1.0, cfg.dtype, device)
+    k = _normal(gen, (tk, cfg.Hkv, cfg.D), 1.0, cfg.dtype, device)
+    v = _normal(gen, (tk, cfg.Hkv, cfg.D), 1.0, cfg.dtype, device)
+    cu = lambda lens: torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32,
+                                   device=device)
+    return q, k, v, cu(cfg.q_lens), cu(cfg.k_lens)
