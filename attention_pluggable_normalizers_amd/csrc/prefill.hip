@@ -38,12 +38,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D_, int BN_, int NW_, bool PIPE_ = false>
+template <int D_, int BN_, int NW_>
 struct Cfg {
   static constexpr int D = D_, BN = BN_, NW = NW_;
-  // softmax family: three LDS tile buffers, and the scores of tile t + 1 are
-  // computed before the weights of tile t (matrix cores and vector ALUs overlap)
-  static constexpr bool PIPE = PIPE_;
   static constexpr int NT = NW * 64;          // threads per workgroup
   static constexpr int BM = NW * 32;          // query rows per workgroup
   static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
@@ -350,12 +347,133 @@ __device__ __forceinline__ float capped_log2(float raw, float sc_over_cap, float
 // stay <= 2^kRescale.  The true running max is tracked for row_stats.
 constexpr float kRescale = 8.f;
 
-template <class C, int NORM, bool CAP>
+// Direct global -> LDS staging for the softmax family (buffer_load ... lds):
+// no staging registers and no vector-ALU work, so NBUF tiles can be in flight.
+// One transfer moves 1 KB per wave; lane l's 16 bytes land at byte 16 l of
+// the destination, and the lane's source chunk is chosen so that the LDS
+// image of a tile is row-major with an XOR chunk swizzle:
+//   K: chunk c of key r at position c ^ (r & 7)      (the k_chunk swizzle)
+//   V: chunk c of key r at position c ^ v_swz(r)
+// Keys past the end of the sequence read as zeros (buffer range check, which
+// covers the scalar offset too); a transfer that is not needed is sent wholly
+// out of range, so every wave issues the same number per tile.
+//
+// The transfer is issued from inline assembly, so the compiler neither sees
+// it as an LDS write nor counts it: every wait for it is explicit (wait_vmcnt
+// before the barrier that publishes a tile).  Left to the compiler, a
+// transposing LDS read would wait for all transfers in flight, the prefetch
+// included.  Compiler-counted waits stay correct, since vector-memory loads
+// complete in issue order and extra loads only make a vmcnt wait stricter.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, num_records = bytes) in scalar registers.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+               __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff + soff to LDS byte lds_addr + 16 l.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+template <class C>
+__device__ __forceinline__ int v_swz(int r) { return C::D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
+
+// s_waitcnt for "at most N vector-memory operations of this wave in flight"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads()
+// (which would wait for every transfer in flight); LDS hazards are covered by
+// explicit vmcnt waits and by each wave consuming its LDS reads before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <class C>
+struct DmaTiles {
+  static constexpr int NI = C::KCH / 64 / C::NW;  // transfers per wave per K (and per V) tile
+  static_assert(C::KCH % (64 * C::NW) == 0, "K/V tile must split into 1 KB transfers per wave");
+  static constexpr int PER_TILE = 2 * NI;         // vmcnt events per tile
+  uint32_t ko[NI], vo[NI];                        // per-lane byte offsets inside a tile
+  uint32_t kstr, vstr;
+  int wave;                                       // wave-uniform
+
+  __device__ __forceinline__ void init(int64_t ksl, int64_t vsl, int wave_u, int lane) {
+    kstr = (uint32_t)(ksl * 2);
+    vstr = (uint32_t)(vsl * 2);
+    wave = wave_u;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = (i * C::NW + wave) * 64 + lane;  // LDS chunk this lane fills
+      const int row = pos / C::CPR, pc = pos % C::CPR;
+      ko[i] = row * kstr + (pc ^ (row & 7)) * 16;
+      vo[i] = row * vstr + (pc ^ v_swz<C>(row)) * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(i32x4 rk, i32x4 rv, const bf16_t* kl, const bf16_t* vl, int k0,
+                                        bool live) {
+    const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
+    const uint32_t vs = live ? (uint32_t)k0 * vstr : 0x80000000u;
+    const uint32_t kla = lds_addr(kl) + wave * 1024, vla = lds_addr(vl) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
+      dma16(rv, vla + i * C::NW * 1024, vo[i], vs);
+    }
+  }
+};
+
+// V^T operand (32 dims x 16 keys) of PV step t and dim block db, read from a
+// row-major V tile by two transposing LDS reads (ds_read_b64_tr_b16).  In each
+// group of 16 lanes, source lane 4 j + q names 4 dims of key j and result
+// lane i receives dim i of the 4 keys; the groups are placed so that lane
+// (d, half g) ends with the keys 4g..4g+3 and 8+4g..8+4g+3 of the step, the
+// keys its half of the P operand holds (S^T accumulator layout).
+template <class C>
+struct VTr {
+  uint32_t off[C::NDB];  // byte offset of this lane's first read for step 0
+  __device__ __forceinline__ void init(int lane) {
+    const int G = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+    const int r0 = 4 * (G >> 1) + j;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int lc = db * 4 + 2 * (G & 1) + (q >> 1);
+      off[db] = (uint32_t)((r0 * C::D + (lc ^ v_swz<C>(r0)) * 8 + (q & 1) * 4) * 2);
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16_t* vl, int t, int db) const {
+    const char* p = (const char*)vl + off[db] + t * 16 * C::D * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p + 8 * C::D * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+template <class C, int NBUF, int NORM, bool CAP>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_kernel(FwdArgs a) {
-  constexpr int NBUF = C::PIPE ? 3 : 2;
+  static_assert(NBUF == 2 || NBUF == 3, "two or three tiles in flight");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NBUF * 2 * C::BN * C::D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   int bh, qb;
@@ -377,9 +495,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const int klo = first.lo, khi = last.hi;
   const int t0 = klo / C::BN;
   const int t1 = khi > klo ? (khi + C::BN - 1) / C::BN : t0;
-  // LDS buffer of tile u: K [BN][D] then V^T [D][BN]
-  auto kl_of = [&](int u) { return lds + ((u - t0) % NBUF) * 2 * C::BN * C::D; };
-  auto vl_of = [&](int u) { return lds + ((u - t0) % NBUF) * 2 * C::BN * C::D + C::BN * C::D; };
+  // LDS stage u: K [BN][D] then V [BN][D], both row-major and swizzled
+  auto kl_of = [&](int u) { return lds + u * 2 * C::BN * C::D; };
+  auto vl_of = [&](int u) { return lds + u * 2 * C::BN * C::D + C::BN * C::D; };
 
   // this wave's rows and this lane's row
   const int wq0 = q0 + 32 * wave;
@@ -416,14 +534,21 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const float c2 = a.scaling * kLog2e;
   const float sc_over_cap = CAP ? a.scaling / a.softcap : 0.f;
   const float cap_log2e = CAP ? a.softcap * kLog2e : 0.f;
+  VTr<C> vtr;
+  vtr.init(lane);
 
   // weights of one tile from its raw scores s, then O += V^T P^T
-  auto consume = [&](f32x16 (&s)[C::NKB], int t) __attribute__((always_inline)) {
+  auto consume = [&](f32x16 (&s)[C::NKB], int t, const bf16_t* vl) __attribute__((always_inline)) {
     const int k0 = t * C::BN;
-    const bf16_t* vl = vl_of(t);
-    constexpr bool kPreV = VOps<C>::N <= 8;  // V operands fit in registers across the softmax
-    VOps<C> vo;
-    if constexpr (kPreV) vo.read(vl, l32, g);
+    constexpr int NV = C::NDB * 2 * C::NKB;
+    constexpr bool kPreV = NV <= 8;  // V operands fit in registers across the softmax
+    bf16x8 vop[kPreV ? NV : 1];
+    if constexpr (kPreV) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int u = 0; u < 2 * C::NKB; ++u) vop[db * 2 * C::NKB + u] = vtr.read(vl, u, db);
+    }
     if (CAP) {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
@@ -476,61 +601,42 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
       pk[2 * kb + 1] = p_operand(p + 8);
     }
     lsum += ps;
-    if constexpr (kPreV)
-      pv_tile_ops<C>(vo, pk, o);
-    else
-      pv_tile<C>(vl, pk, l32, g, o);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2 * C::NKB; ++u)
+        o[db] = mfma(kPreV ? vop[db * 2 * C::NKB + u] : vtr.read(vl, u, db), pk[u], o[db]);
   };
 
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
-  Tiles<C> tiles;
-  tiles.init(a.k_sl, a.v_sl, tid);
+  const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
+  const i32x4 rv = rsrc_words(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
+  DmaTiles<C> dma;
+  dma.init(a.k_sl, a.v_sl, wave, lane);
+  constexpr int kAhead = (NBUF - 2) * DmaTiles<C>::PER_TILE;  // transfers left in flight at a wait
 
-  if constexpr (!C::PIPE) {
-    if (t0 < t1) {
-      tiles.load(rk, rv, t0 * C::BN);
-      tiles.store(kl_of(t0), vl_of(t0), tid);
+  // tile t lives in stage (t - t0) % NBUF; stages of tiles t0 .. t0 + NBUF - 2 first
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) dma.issue(rk, rv, kl_of(u), vl_of(u), (t0 + u) * C::BN, t0 + u < t1);
+  // everything, the Q loads included: the compiler then knows Q is in
+  // registers and places no vmcnt wait inside the loop
+  wait_vmcnt<0>();
+  lds_barrier();
+  int cur = 0;
+  for (int t = t0; t < t1; ++t) {
+    // the stage of tile t + NBUF - 1 held tile t - 1, whose reads all ended
+    // before the barrier that closed the previous step
+    const int nxt = cur == 0 ? NBUF - 1 : cur - 1;
+    dma.issue(rk, rv, kl_of(nxt), vl_of(nxt), (t + NBUF - 1) * C::BN, t + NBUF - 1 < t1);
+    if (tile_active(t)) {
+      f32x16 s[C::NKB];
+      qk_tile<C>(kl_of(cur), qreg, l32, g, s);
+      consume(s, t, vl_of(cur));
     }
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-      if (t + 1 < t1) tiles.load(rk, rv, (t + 1) * C::BN);
-      if (tile_active(t)) {
-        f32x16 s[C::NKB];
-        qk_tile<C>(kl_of(t), qreg, l32, g, s);
-        consume(s, t);
-      }
-      if (t + 1 < t1) tiles.store(kl_of(t + 1), vl_of(t + 1), tid);
-      __syncthreads();
-    }
-  } else {
-    // tiles t and t + 1 are in LDS while tile t + 2 is loaded; the scores of
-    // tile t + 1 are issued to the matrix cores before tile t's weights are
-    // computed on the vector ALUs.  Buffer of tile t + 2 = that of tile t - 1,
-    // whose last reads (its V) precede the barrier ending step t - 1.
-    for (int u = t0; u < min(t0 + 2, t1); ++u) {
-      tiles.load(rk, rv, u * C::BN);
-      tiles.store(kl_of(u), vl_of(u), tid);
-    }
-    __syncthreads();
-    f32x16 sa[C::NKB], sb[C::NKB];
-    bool act_a = t0 < t1 && tile_active(t0), act_b = false;
-    if (act_a) qk_tile<C>(kl_of(t0), qreg, l32, g, sa);
-    auto step = [&](f32x16 (&cur)[C::NKB], bool act_cur, f32x16 (&nxt)[C::NKB], bool& act_nxt, int t)
-        __attribute__((always_inline)) {
-      if (t + 2 < t1) tiles.load(rk, rv, (t + 2) * C::BN);
-      act_nxt = t + 1 < t1 && tile_active(t + 1);
-      if (act_nxt) qk_tile<C>(kl_of(t + 1), qreg, l32, g, nxt);
-      if (act_cur) consume(cur, t);
-      if (t + 2 < t1) tiles.store(kl_of(t + 2), vl_of(t + 2), tid);
-      __syncthreads();
-    };
-    for (int t = t0; t < t1; t += 2) {
-      step(sa, act_a, sb, act_b, t);
-      if (t + 1 >= t1) break;
-      step(sb, act_b, sa, act_a, t + 1);
-    }
+    wait_vmcnt<kAhead>();  // this wave's part of tile t + 1 has landed
+    lds_barrier();
+    cur = cur == NBUF - 1 ? 0 : cur + 1;
   }
+  wait_vmcnt<0>();  // no transfer may outlive the workgroup's LDS
 
   // epilogue
   const float ltot = pair_sum(lsum);
@@ -1205,6 +1311,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   }
 }
 
+// K/V tiles in flight per workgroup (LDS: NBUF * 2 * BN * D * 2 bytes)
+template <class C>
+constexpr int kStages = C::D == 64 ? 3 : 2;
+
 template <class C, int NORM>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
@@ -1217,9 +1327,9 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
       prefill_sparse_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
   } else {
     if (cap)
-      prefill_softmax_kernel<C, NORM, true><<<grid, block, 0, stream>>>(a);
+      prefill_softmax_kernel<C, kStages<C>, NORM, true><<<grid, block, 0, stream>>>(a);
     else
-      prefill_softmax_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
+      prefill_softmax_kernel<C, kStages<C>, NORM, false><<<grid, block, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
