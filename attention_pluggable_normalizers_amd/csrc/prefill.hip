@@ -1,8 +1,9 @@
 // Tiled bf16 prefill on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // One workgroup owns BM = 32 * NW query rows of one (batch, query head); each
-// wave owns 32 rows.  K/V tiles of BN keys stream through LDS (double
-// buffered), shared by the waves.  Per tile and wave:
+// wave owns 32 rows.  K/V tiles of BN keys go from global memory straight
+// into LDS (two to three tiles in flight), shared by the waves.  Per tile and
+// wave:
 //
 //   S^T (keys x queries) = K_tile . Q^T      A = K rows (LDS), B = Q (registers)
 //   O^T (d x queries)   += V_tile^T . P^T    A = V^T (LDS),   B = P (registers)
@@ -12,7 +13,8 @@
 // row reductions of the normalizer are in-lane plus one exchange with the
 // partner lane, and the probabilities P leave the S accumulators already in
 // the register layout the PV product consumes.  The contraction of the PV
-// product runs over keys, so V is transposed while it is staged into LDS.
+// product runs over keys: V stays row-major in LDS and its transposed operand
+// comes from the transposing LDS read (ds_read_b64_tr_b16).
 //
 // Masking is computed, never stored: the workgroup visits only key tiles
 // inside its causal / window bounds ("Attention variants": a kernel that
@@ -45,14 +47,9 @@ struct Cfg {
   static constexpr int BM = NW * 32;          // query rows per workgroup
   static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
   static constexpr int KCH = BN * CPR;        // chunks per K tile
-  static constexpr int KPT = KCH / NT;        // K chunks per thread
-  static constexpr int VUN = (BN / 4) * CPR;  // V staging units (4 keys x 8 dims)
-  static constexpr int VPT = (VUN + NT - 1) / NT;
   static constexpr int NKB = BN / 32;         // 32-key blocks per tile
   static constexpr int NDB = D / 32;          // 32-dim blocks of the output
   static constexpr int NQC = D / 16;          // 16-dim steps of QK^T
-  static constexpr int VSW = (BN / 8 >= 8) ? 7 : (BN / 8 - 1);  // V^T chunk swizzle mask
-  static_assert(KCH % NT == 0, "K tile must split evenly over the threads");
   static_assert(CPR >= 8, "head dim must be >= 64");
   static_assert(BN % 32 == 0, "BN must be a multiple of 32");
 };
@@ -63,20 +60,15 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
 
-// Position of tile key kk inside a V^T row.  Within each group of 16 keys the
-// order is 0-3, 8-11, 4-7, 12-15: the 8 keys one lane half feeds to a PV
-// step are then contiguous (see the S^T accumulator layout).
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int q = (kk >> 2) & 3;  // which group of 4 inside the 16
-  const int sw = (q == 1) ? 2 : (q == 2 ? 1 : q);
-  return (kk & ~15) | (sw << 2) | (kk & 3);
+// XOR swizzle of 16-byte chunks inside an LDS row of K.  The 64 LDS banks
+// (256 bytes) serve 16 lanes of a 16-byte read per cycle, and those lanes
+// read 16 consecutive rows at one logical chunk: with 128-byte rows (D = 64)
+// rows of equal parity share a bank window, so the chunk is XORed with
+// (row / 2) mod 8; with rows of 256 bytes or more, with row mod 16.
+template <int D>
+__device__ __forceinline__ int k_chunk(int row, int ch) {
+  return ch ^ (D == 64 ? (row >> 1) & 7 : row & 15);
 }
-
-// XOR swizzle of 16-byte chunks inside an LDS row (spreads the 32 rows a
-// wave reads at one column over distinct banks).
-__device__ __forceinline__ int k_chunk(int row, int ch) { return ch ^ (row & 7); }
-template <int VSW>
-__device__ __forceinline__ int v_chunk(int d, int ch) { return ch ^ ((d ^ (d >> 3)) & VSW); }
 
 struct RowBounds {
   int lo, hi;  // visible keys [lo, hi) of one query row
@@ -138,106 +130,6 @@ __device__ __forceinline__ SeqSpan seq_span(const FwdArgs& a, int b, int h) {
   return s;
 }
 
-// Buffer resource over `bytes` bytes at `base`: raw buffer loads past the end
-// return zeros, which is how the ragged last key tile is read.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-
-// Global -> register -> LDS staging of one K tile (row-major, chunk-swizzled)
-// and one V tile (transposed).  Every thread loads KPT 16-byte K chunks and
-// VPT units of KPU keys x 8 dims of V.  Row strides are in bytes.
-template <class C>
-struct Tiles {
-  static constexpr int KPU = ((C::BN / 4) * C::CPR >= C::NT) ? 4 : 2;
-  static constexpr int VUN = (C::BN / KPU) * C::CPR;
-  static constexpr int VPT = VUN / C::NT;
-  static_assert(VUN % C::NT == 0, "V tile must split evenly over the threads");
-  static constexpr int KROWS = C::NT / C::CPR;  // K rows covered by one pass of the threads
-  static constexpr int VROWS = KROWS * KPU;     // V rows covered by one pass of the threads
-
-  u32x4 kr[C::KPT];
-  u32x4 vr[VPT][KPU];
-  uint32_t kvoff, vvoff;  // per-thread byte offsets inside a tile
-  uint32_t kstr, vstr;    // row strides in bytes
-
-  __device__ __forceinline__ void init(int64_t ksl, int64_t vsl, int tid) {
-    kstr = (uint32_t)(ksl * 2);
-    vstr = (uint32_t)(vsl * 2);
-    const int r = tid / C::CPR, ch = tid % C::CPR;
-    kvoff = r * kstr + ch * 16;
-    vvoff = r * KPU * vstr + ch * 16;
-  }
-  __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int k0) {
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) kr[i] = buf_load16(rk, kvoff, (k0 + i * KROWS) * kstr);
-  }
-  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, int k0) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-      for (int j = 0; j < KPU; ++j) vr[i][j] = buf_load16(rv, vvoff, (k0 + i * VROWS + j) * vstr);
-  }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k0) {
-    load_k(rk, k0);
-    load_v(rv, k0);
-  }
-
-  __device__ __forceinline__ void store_k(bf16_t* kl, int tid) {
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::CPR, ch = id % C::CPR;
-      *(u32x4*)(kl + row * C::D + k_chunk(row, ch) * 8) = kr[i];
-    }
-  }
-
-  __device__ __forceinline__ void store_v(bf16_t* vl, int tid) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = tid + i * C::NT;
-      const int kg = id / C::CPR, ch = id % C::CPR;
-      const int pos = vt_pos(kg * KPU);
-      const int pch = pos >> 3, poff = pos & 7;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {  // dword w of each key row = dims 2w, 2w+1
-#pragma unroll
-        for (int hbit = 0; hbit < 2; ++hbit) {
-          const int d = ch * 8 + 2 * w + hbit;
-          bf16_t* dst = vl + d * C::BN + v_chunk<C::VSW>(d, pch) * 8 + poff;
-          if constexpr (KPU == 4) {
-            const unsigned a0 = vr[i][0][w], a1 = vr[i][1][w], a2 = vr[i][2][w], a3 = vr[i][3][w];
-            u32x2 val;
-            if (hbit == 0) {
-              val[0] = (a0 & 0xffffu) | (a1 << 16);
-              val[1] = (a2 & 0xffffu) | (a3 << 16);
-            } else {
-              val[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-              val[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            }
-            *(u32x2*)dst = val;
-          } else {
-            const unsigned a0 = vr[i][0][w], a1 = vr[i][1][w];
-            *(unsigned*)dst = hbit == 0 ? ((a0 & 0xffffu) | (a1 << 16))
-                                        : ((a0 >> 16) | (a1 & 0xffff0000u));
-          }
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16_t* kl, bf16_t* vl, int tid) {
-    store_k(kl, tid);
-    store_v(vl, tid);
-  }
-};
-
-// S^T accumulators of one tile for this wave: s[kb][r] is the raw q.k of key
-// k0 + 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 and query lane % 32.
 template <class C>
 __device__ __forceinline__ void qk_tile(const bf16_t* kl, const bf16x8* qreg, int l32, int g,
                                         f32x16* s) {
@@ -253,7 +145,7 @@ __device__ __forceinline__ void qk_tile(const bf16_t* kl, const bf16x8* qreg, in
     for (int j = 0; j < QG; ++j) {
       const int c = (g0 + j) / C::NKB, kb = (g0 + j) % C::NKB;
       const int row = kb * 32 + l32;
-      kv[j] = *(const bf16x8*)(kl + row * C::D + k_chunk(row, 2 * c + g) * 8);
+      kv[j] = *(const bf16x8*)(kl + row * C::D + k_chunk<C::D>(row, 2 * c + g) * 8);
     }
 #pragma unroll
     for (int j = 0; j < QG; ++j) {
@@ -261,46 +153,6 @@ __device__ __forceinline__ void qk_tile(const bf16_t* kl, const bf16x8* qreg, in
       s[kb] = mfma(kv[j], qreg[c], s[kb]);
     }
   }
-}
-
-// V^T operands of a whole tile for this lane (read before the softmax work
-// so the LDS latency hides behind it).
-template <class C>
-struct VOps {
-  static constexpr int N = C::NDB * 2 * C::NKB;
-  bf16x8 v[N];
-  __device__ __forceinline__ void read(const bf16_t* vl, int l32, int g) {
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const int d = db * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < 2 * C::NKB; ++t)
-        v[db * 2 * C::NKB + t] = *(const bf16x8*)(vl + d * C::BN + v_chunk<C::VSW>(d, 2 * t + g) * 8);
-    }
-  }
-};
-
-template <class C>
-__device__ __forceinline__ void pv_tile(const bf16_t* vl, const bf16x8* pk, int l32, int g,
-                                        f32x16* o) {
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    const int d = db * 32 + l32;
-    bf16x8 vv[2 * C::NKB];
-#pragma unroll
-    for (int t = 0; t < 2 * C::NKB; ++t)
-      vv[t] = *(const bf16x8*)(vl + d * C::BN + v_chunk<C::VSW>(d, 2 * t + g) * 8);
-#pragma unroll
-    for (int t = 0; t < 2 * C::NKB; ++t) o[db] = mfma(vv[t], pk[t], o[db]);
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void pv_tile_ops(const VOps<C>& vo, const bf16x8* pk, f32x16* o) {
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int t = 0; t < 2 * C::NKB; ++t) o[db] = mfma(vo.v[db * 2 * C::NKB + t], pk[t], o[db]);
 }
 
 __device__ __forceinline__ int s_key(int k0, int kb, int r, int g) {
@@ -352,7 +204,7 @@ constexpr float kRescale = 8.f;
 // One transfer moves 1 KB per wave; lane l's 16 bytes land at byte 16 l of
 // the destination, and the lane's source chunk is chosen so that the LDS
 // image of a tile is row-major with an XOR chunk swizzle:
-//   K: chunk c of key r at position c ^ (r & 7)      (the k_chunk swizzle)
+//   K: chunk c of key r at position k_chunk(r, c)
 //   V: chunk c of key r at position c ^ v_swz(r)
 // Keys past the end of the sequence read as zeros (buffer range check, which
 // covers the scalar offset too); a transfer that is not needed is sent wholly
@@ -423,9 +275,15 @@ struct DmaTiles {
     for (int i = 0; i < NI; ++i) {
       const int pos = (i * C::NW + wave) * 64 + lane;  // LDS chunk this lane fills
       const int row = pos / C::CPR, pc = pos % C::CPR;
-      ko[i] = row * kstr + (pc ^ (row & 7)) * 16;
+      ko[i] = row * kstr + k_chunk<C::D>(row, pc) * 16;
       vo[i] = row * vstr + (pc ^ v_swz<C>(row)) * 16;
     }
+  }
+  __device__ __forceinline__ void issue_k(i32x4 rk, const bf16_t* kl, int k0, bool live) {
+    const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
+    const uint32_t kla = lds_addr(kl) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
   }
   __device__ __forceinline__ void issue(i32x4 rk, i32x4 rv, const bf16_t* kl, const bf16_t* vl, int k0,
                                         bool live) {
@@ -692,12 +550,20 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 // to one.
 // ---------------------------------------------------------------------------
 
+// LDS of the sparse kernel (dynamic): NA K stages for the threshold passes,
+// then the candidate buffers; the output pass reuses all of it for NB K/V
+// stages.  Two workgroups per CU below D = 256 (their register use allows no
+// more), one at D = 256.
 template <class C>
 struct SparseCfg {
-  static constexpr int REGION_BYTES = 65536 - 2 * C::BN * C::D * 2;  // V tiles / candidates
-  static constexpr int SCAP = REGION_BYTES / (C::NT * 4);            // candidates per lane
-  static_assert(REGION_BYTES >= 2 * C::BN * C::D * 2, "region must hold two V tiles");
-  static_assert(SCAP >= 32 && SCAP % 8 == 0, "candidate buffer too small");
+  static constexpr int LDS_BYTES = C::D == 256 ? 160 * 1024 : 80 * 1024;
+  static constexpr int NA = 3;                     // K tiles in flight, threshold passes
+  static constexpr int NB = 3;                     // K/V tiles in flight, output pass
+  static constexpr int KTILE = C::BN * C::D * 2;   // bytes of one K (or V) tile
+  static constexpr int REGION_BYTES = LDS_BYTES - NA * KTILE;  // candidate buffers
+  static constexpr int SCAP = REGION_BYTES / (C::NT * 4) / 8 * 8;  // candidates per lane
+  static_assert(NB * 2 * KTILE <= LDS_BYTES, "output pass stages must fit");
+  static_assert(SCAP >= 32, "candidate buffer too small");
 };
 
 // z of one raw score q.k (the value the threshold acts on).
@@ -848,11 +714,14 @@ template <class C, int NORM, bool CAP>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_kernel(FwdArgs a) {
   using SC = SparseCfg<C>;
   constexpr int SCAP = SC::SCAP;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BN * C::D + SC::REGION_BYTES / 2];
-  bf16_t* const kl0 = lds;
-  bf16_t* const vl0 = lds + 2 * C::BN * C::D;
+  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];  // SC::LDS_BYTES
+  constexpr int KT = C::BN * C::D;  // elements of one K or V tile
+  auto ka_of = [&](int u) { return lds + u * KT; };  // threshold passes: K stage u
+  auto kb_of = [&](int u) { return lds + u * 2 * KT; };  // output pass: K stage u ...
+  auto vb_of = [&](int u) { return lds + u * 2 * KT + KT; };  // ... and its V
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   int bh, qb;
@@ -897,7 +766,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   const float capz = CAP ? (ent ? 0.5f * a.softcap : a.softcap) : 0.f;
 
   // ---- pass A: row max, floor and candidates --------------------------------
-  float* const buf = (float*)vl0 + wave * SCAP * 64 + lane;
+  float* const buf = (float*)(lds + SC::NA * KT) + wave * SCAP * 64 + lane;
   float mrun = -INFINITY;     // running max of z over the row (both lanes)
   double floor_ = -INFINITY;  // lower bound on tau (z units)
   float floor_f = -INFINITY;  // largest float <= floor_
@@ -990,19 +859,36 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     }
   };
 
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
-  Tiles<C> tiles;
-  tiles.init(a.k_sl, a.v_sl, tid);
-  if (t0 < t1) {
-    tiles.load_k(rk, t0 * C::BN);
-    tiles.store_k(kl0, tid);
-  }
-  __syncthreads();
+  const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
+  const i32x4 rv = rsrc_words(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
+  DmaTiles<C> dma;
+  dma.init(a.k_sl, a.v_sl, wave, lane);
+  constexpr int NA = SC::NA;
+  // K tiles t0 .. t0 + NA - 2 into stages 0 .. NA - 2; tile t sits in stage
+  // (t - t0) mod NA.  Everything is waited for here, the Q loads included, so
+  // that the compiler needs no vmcnt wait inside the loops.
+  auto k_prologue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NA - 1; ++u) dma.issue_k(rk, ka_of(u), (t0 + u) * C::BN, t0 + u < t1);
+    wait_vmcnt<0>();
+    lds_barrier();
+  };
+  // start of step t: K of tile t + NA - 1 into the stage tile t - 1 left
+  auto k_next = [&](int t, int cur) __attribute__((always_inline)) {
+    const int nxt = cur == 0 ? NA - 1 : cur - 1;
+    dma.issue_k(rk, ka_of(nxt), (t + NA - 1) * C::BN, t + NA - 1 < t1);
+  };
+  // end of step t: this wave's part of tile t + 1 has landed, then the barrier
+  auto k_done = [&](int& cur) __attribute__((always_inline)) {
+    wait_vmcnt<(NA - 2) * DmaTiles<C>::NI>();
+    lds_barrier();
+    cur = cur == NA - 1 ? 0 : cur + 1;
+  };
+  k_prologue();
+  int cur = 0;
   for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    const bf16_t* kl = kl0 + cur * C::BN * C::D;
-    if (t + 1 < t1) tiles.load_k(rk, (t + 1) * C::BN);
+    const bf16_t* kl = ka_of(cur);
+    k_next(t, cur);
     const int k0 = t * C::BN;
     const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
@@ -1093,9 +979,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         }
       }
     }
-    if (t + 1 < t1) tiles.store_k(kl0 + (cur ^ 1) * C::BN * C::D, tid);
-    __syncthreads();
+    k_done(cur);
   }
+  wait_vmcnt<0>();
 
   // ---- exact threshold over the candidates ---------------------------------
   double tau = INFINITY;
@@ -1131,21 +1017,29 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // values above it into the lane buffers.  When both halves fit, the row is
   // solved exactly from the buffers as above; otherwise the totals give one
   // threshold step and the next pass starts from the raised floor.
-  while (__syncthreads_or(pending)) {
+  // workgroup OR through one word of the last K stage (idle here: every
+  // transfer has landed); the runtime's __syncthreads_or would take static LDS
+  // on top of the dynamic allocation and cost the second workgroup per CU
+  int* const any_word = (int*)ka_of(NA - 1);
+  auto block_any = [&](bool v) __attribute__((always_inline)) {
+    __syncthreads();
+    if (tid == 0) *(volatile int*)any_word = 0;
+    __syncthreads();
+    if (v) *(volatile int*)any_word = 1;
+    __syncthreads();
+    return *(volatile int*)any_word != 0;
+  };
+  while (block_any(pending)) {
     double c = 0.0, s1 = 0.0, s2 = 0.0;
     float mn = INFINITY;
     const double mref = (double)mrun;
     cnt = 0;
     int fits = pending ? 1 : 0;
-    if (t0 < t1) {
-      tiles.load_k(rk, t0 * C::BN);
-      tiles.store_k(kl0, tid);
-    }
-    __syncthreads();
+    k_prologue();
+    cur = 0;
     for (int t = t0; t < t1; ++t) {
-      const int cur = (t - t0) & 1;
-      const bf16_t* kl = kl0 + cur * C::BN * C::D;
-      if (t + 1 < t1) tiles.load_k(rk, (t + 1) * C::BN);
+      const bf16_t* kl = ka_of(cur);
+      k_next(t, cur);
       const int k0 = t * C::BN;
       const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(pending);
       if (active) {
@@ -1193,9 +1087,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           }
         }
       }
-      if (t + 1 < t1) tiles.store_k(kl0 + (cur ^ 1) * C::BN * C::D, tid);
-      __syncthreads();
+      k_done(cur);
     }
+    wait_vmcnt<0>();
     c += partner_d(c);
     s1 += partner_d(s1);
     s2 += partner_d(s2);
@@ -1246,16 +1140,23 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   f32x16 o[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
-  if (t0 < t1) {
-    tiles.load(rk, rv, t0 * C::BN);
-    tiles.store(kl0, vl0, tid);
-  }
-  __syncthreads();
+  // the candidate buffers are dead once every wave is past its solve
+  lds_barrier();
+  constexpr int NB = SC::NB;
+  VTr<C> vtr;
+  vtr.init(lane);
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) dma.issue(rk, rv, kb_of(u), vb_of(u), (t0 + u) * C::BN, t0 + u < t1);
+  wait_vmcnt<0>();
+  lds_barrier();
+  cur = 0;
   for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    const bf16_t* kl = kl0 + cur * C::BN * C::D;
-    const bf16_t* vl = vl0 + cur * C::BN * C::D;
-    if (t + 1 < t1) tiles.load(rk, rv, (t + 1) * C::BN);
+    const bf16_t* kl = kb_of(cur);
+    const bf16_t* vl = vb_of(cur);
+    {
+      const int nxt = cur == 0 ? NB - 1 : cur - 1;
+      dma.issue(rk, rv, kb_of(nxt), vb_of(nxt), (t + NB - 1) * C::BN, t + NB - 1 < t1);
+    }
     const int k0 = t * C::BN;
     const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
@@ -1283,11 +1184,18 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           pk[2 * kb + (r >> 3)][r & 7] = pb;
         }
       }
-      if (__any(any)) pv_tile<C>(vl, pk, l32, g, o);
+      if (__any(any)) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int u = 0; u < 2 * C::NKB; ++u) o[db] = mfma(vtr.read(vl, u, db), pk[u], o[db]);
+      }
     }
-    if (t + 1 < t1) tiles.store(kl0 + (cur ^ 1) * C::BN * C::D, vl0 + (cur ^ 1) * C::BN * C::D, tid);
-    __syncthreads();
+    wait_vmcnt<(NB - 2) * DmaTiles<C>::PER_TILE>();
+    lds_barrier();
+    cur = cur == NB - 1 ? 0 : cur + 1;
   }
+  wait_vmcnt<0>();  // no transfer may outlive the workgroup's LDS
 
   const float wtot = wsum + partner(wsum);
   if (row_ok) {
@@ -1321,10 +1229,14 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(nqb * a.B * a.Hq)), block(C::NT);
   const bool cap = a.softcap > 0.f;
   if constexpr (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
-    if (cap)
-      prefill_sparse_kernel<C, NORM, true><<<grid, block, 0, stream>>>(a);
-    else
-      prefill_sparse_kernel<C, NORM, false><<<grid, block, 0, stream>>>(a);
+    constexpr int lds = SparseCfg<C>::LDS_BYTES;
+    auto go = [&](auto kern) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      kern<<<grid, block, lds, stream>>>(a);
+      return hipGetLastError();
+    };
+    return cap ? go(prefill_sparse_kernel<C, NORM, true>) : go(prefill_sparse_kernel<C, NORM, false>);
   } else {
     if (cap)
       prefill_softmax_kernel<C, kStages<C>, NORM, true><<<grid, block, 0, stream>>>(a);
@@ -1338,7 +1250,12 @@ template <int NORM>
 hipError_t launch_norm(const FwdArgs& a, hipStream_t stream) {
   switch (a.D) {
     case 64: return launch_cfg<Cfg<64, 64, 4>, NORM>(a, stream);
-    case 128: return launch_cfg<Cfg<128, 64, 4>, NORM>(a, stream);
+    case 128:
+      // the sparse kernel takes 32-key tiles: more LDS left for candidates
+      if constexpr (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15)
+        return launch_cfg<Cfg<128, 32, 4>, NORM>(a, stream);
+      else
+        return launch_cfg<Cfg<128, 64, 4>, NORM>(a, stream);
     default: return launch_cfg<Cfg<256, 32, 4>, NORM>(a, stream);
   }
 }
