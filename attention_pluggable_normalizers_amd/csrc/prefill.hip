@@ -58,7 +58,15 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
+// Value held by the partner lane (l ^ 32), through v_permlane32_swap (no LDS
+// round trip).  The swap returns this lane's value and the partner's in its
+// two result slots; the slot that differs from the own value is the
+// partner's (if the two are equal the choice does not matter).
+__device__ __forceinline__ unsigned partner_u(unsigned x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] == x ? r[1] : r[0];
+}
+__device__ __forceinline__ float partner(float x) { return __uint_as_float(partner_u(__float_as_uint(x))); }
 
 // XOR swizzle of 16-byte chunks inside an LDS row of K.  The 64 LDS banks
 // (256 bytes) serve 16 lanes of a 16-byte read per cycle, and those lanes
@@ -191,6 +199,20 @@ __device__ __forceinline__ float capped_log2(float raw, float sc_over_cap, float
   const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);  // exp(2y)
   const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);  // tanh(y)
   return cap_log2e * t;
+}
+
+// z of one raw score q.k (the value the threshold acts on).
+// Monotone in raw (cz, capz > 0); a masked score (-inf) stays -inf.
+template <bool CAP>
+__device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, float capz) {
+#pragma clang fp contract(off)
+  if (CAP) {
+    const float y = raw * sc_over_cap;
+    const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
+    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
+    return raw == -INFINITY ? -INFINITY : capz * t;
+  }
+  return raw * cz;
 }
 
 // Lazy rescaling: the accumulators O and l are kept relative to a reference
@@ -566,20 +588,6 @@ struct SparseCfg {
   static_assert(SCAP >= 32, "candidate buffer too small");
 };
 
-// z of one raw score q.k (the value the threshold acts on).
-// Monotone in raw (cz, capz > 0); a masked score (-inf) stays -inf.
-template <bool CAP>
-__device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, float capz) {
-#pragma clang fp contract(off)
-  if (CAP) {
-    const float y = raw * sc_over_cap;
-    const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
-    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
-    return raw == -INFINITY ? -INFINITY : capz * t;
-  }
-  return raw * cz;
-}
-
 __device__ __forceinline__ float max16(const f32x16& v) {
   float m = v[0];
 #pragma unroll
@@ -612,8 +620,16 @@ __device__ __forceinline__ void mask_tile(f32x16* s, int base, int span) {
     }
 }
 
-__device__ __forceinline__ double partner_d(double x) { return __shfl_xor(x, 32, 64); }
-__device__ __forceinline__ int partner_i(int x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ double partner_d(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
+  const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const bool own0 = rl[0] == lo && rh[0] == hi;
+  const unsigned plo = own0 ? rl[1] : rl[0], phi = own0 ? rh[1] : rh[0];
+  return __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
+}
+__device__ __forceinline__ int partner_i(int x) { return (int)partner_u((unsigned)x); }
 
 // One step of the threshold search from lower bound t over the candidate set
 // L = {z > t} with row totals (count c, sum and sum of squares of z - mref,
@@ -660,25 +676,65 @@ __device__ __forceinline__ float float_floor(double x) {
   return f;
 }
 
-// Keeps this lane's candidates above t (compacting them) and returns their
-// partial sums of y = z - mref.  Entries are read 8 at a time so their LDS
-// latencies overlap (SCAP is a multiple of 8, so the reads stay inside the
-// lane's buffer); compaction only writes to slots already read.
-template <int SCAP>
-__device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double mref, double& c,
-                                         double& s1, double& s2, float& mn) {
+// Candidates are stored in the domain of the score test: the raw score q.k
+// without softcap (z = fl(raw * cz) is monotone in raw, so a raw threshold
+// decides z > floor exactly and the product is only formed when a candidate
+// is read), z itself with softcap.
+//
+// Largest float r with fl(r * cz) <= f, for cz > 0: then, for every float
+// raw, fl(raw * cz) > f exactly when raw > r.  Starts from f / cz (within an
+// ulp or two of r) and steps by ulps with the same multiply the scores use.
+__device__ __forceinline__ float next_up(float x) {
+  const unsigned u = __float_as_uint(x);
+  return x == 0.f ? __uint_as_float(1u) : __uint_as_float(x > 0.f ? u + 1u : u - 1u);
+}
+__device__ __forceinline__ float next_down(float x) {
+  const unsigned u = __float_as_uint(x);
+  return x == 0.f ? __uint_as_float(0x80000001u) : __uint_as_float(x > 0.f ? u - 1u : u + 1u);
+}
+__device__ __forceinline__ float raw_floor(float f, float cz) {
+#pragma clang fp contract(off)
+  if (!(f > -INFINITY) || !(f < INFINITY)) return f;  // -inf: every finite raw passes; +inf: none
+  float r = f / cz;
+  if (!(r > -INFINITY && r < INFINITY)) return -INFINITY;  // out of range: let everything through
+  for (int i = 0; i < 8 && r * cz > f; ++i) r = next_down(r);
+  if (r * cz > f) return -INFINITY;  // (cannot happen) stay on the safe side: admit more
+  for (int i = 0; i < 8; ++i) {
+    const float u = next_up(r);
+    if (!(u * cz <= f)) break;
+    r = u;
+  }
+  return r;
+}
+
+template <bool CAP>
+__device__ __forceinline__ float stored_z(float v, float cz) {
+#pragma clang fp contract(off)
+  return CAP ? v : v * cz;
+}
+
+// Keeps this lane's candidates with z above t (compacting them) and returns
+// their partial sums of y = z - mref.  Entries are read 8 at a time so their
+// LDS latencies overlap (SCAP is a multiple of 8, so the reads stay inside
+// the lane's buffer); compaction only writes to slots already read.
+template <int SCAP, bool CAP>
+__device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double mref, float cz,
+                                         double& c, double& s1, double& s2, float& mn) {
   static_assert(SCAP % 8 == 0, "buffer length must be a multiple of 8");
   int w = 0;
   c = s1 = s2 = 0.0;
   mn = INFINITY;
   for (int e0 = 0; e0 < cnt; e0 += 8) {
-    float z[8];
+    float v[8], z[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) z[j] = buf[(e0 + j) * 64];
+    for (int j = 0; j < 8; ++j) {
+      v[j] = buf[(e0 + j) * 64];
+      z[j] = stored_z<CAP>(v[j], cz);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (e0 + j < cnt && (double)z[j] > t) {
-        buf[w * 64] = z[j];
+        buf[w * 64] = v[j];
         ++w;
         const double y = (double)z[j] - mref;
         c += 1.0;
@@ -691,7 +747,8 @@ __device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double 
   cnt = w;
 }
 
-// Keeps this lane's candidates above t (compacting them in place).
+// Keeps this lane's candidates above t, a threshold in the stored domain
+// (compacting them in place).
 template <int SCAP>
 __device__ __forceinline__ void compact_buf(float* buf, int& cnt, float t) {
   int w = 0;
@@ -770,6 +827,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   float mrun = -INFINITY;     // running max of z over the row (both lanes)
   double floor_ = -INFINITY;  // lower bound on tau (z units)
   float floor_f = -INFINITY;  // largest float <= floor_
+  float floor_v = -INFINITY;  // the same test in the stored domain: v > floor_v <=> z > floor_f
+  auto set_floor = [&](double f) __attribute__((always_inline)) {
+    floor_ = f;
+    floor_f = float_floor(f);
+    floor_v = CAP ? floor_f : raw_floor(floor_f, cz);
+  };
   int cnt = 0;                // this lane's candidates
   bool ovf = !row_ok;         // row left to the extra passes (or no row at all)
   bool settled = false;       // floor has reached the exact threshold of the keys seen once
@@ -791,39 +854,51 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       top[i] = hi;
     }
   };
-  // Threshold of the row's 2 kTop listed values (a lower bound when the
-  // steps do not settle).  Wave-uniform: partner exchanges.  Both lanes of a
-  // row order the values alike, so they compute the same floor.
+  // Threshold of the row's 2 kTop listed values (both lanes): a lower bound
+  // on tau.  The two descending lists merge into one (bitonic merge: own list
+  // descending, partner's reversed), then the closed form over each prefix
+  // of m largest values is consistent for the subset's support size, and the
+  // largest consistent one is the subset's threshold (sparsemax: (S_m - 1) / m
+  // with S_m the prefix sum; 1.5-entmax: mean - sqrt((1 - ss) / m) with ss the
+  // prefix's sum of squared deviations, invalid once ss > 1, which only grows
+  // with m).  Both lanes of a row see the same union, so they agree.
   auto top_floor = [&]() __attribute__((always_inline)) -> double {
-    float u[2 * kTop];
+    constexpr int M = 2 * kTop;
+    float u[M];
 #pragma unroll
     for (int i = 0; i < kTop; ++i) {
-      const float o = partner(top[i]);
-      u[i] = g == 0 ? top[i] : o;
-      u[kTop + i] = g == 0 ? o : top[i];
+      u[i] = top[i];
+      u[M - 1 - i] = partner(top[i]);
     }
-    const double mref = (double)fmaxf(u[0], u[kTop]);
-    double t = mref - 1.0;
-    for (int it = 0; it < 2 * kTop + 2; ++it) {
-      double c = 0.0, s1 = 0.0, s2 = 0.0;
-      float mn = INFINITY;
 #pragma unroll
-      for (int i = 0; i < 2 * kTop; ++i) {
-        if ((double)u[i] > t) {
-          const double y = (double)u[i] - mref;
-          c += 1.0;
-          s1 += y;
-          s2 += y * y;
-          mn = fminf(mn, u[i]);
+    for (int span = M / 2; span >= 1; span >>= 1)
+#pragma unroll
+      for (int i = 0; i < M; ++i)
+        if ((i & span) == 0) {
+          const float hi = fmaxf(u[i], u[i + span]), lo = fminf(u[i], u[i + span]);
+          u[i] = hi;
+          u[i + span] = lo;
         }
+    const double mref = (double)u[0];
+    double best = -INFINITY, s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int m = 1; m <= M; ++m) {
+      if (!(u[m - 1] > -INFINITY)) break;
+      const double y = (double)u[m - 1] - mref;
+      s1 += y;
+      s2 += y * y;
+      double t;
+      if (NORM == ATTN_SPARSEMAX) {
+        t = (s1 - 1.0) / m;
+      } else {
+        const double mu = s1 / m;
+        const double d = (1.0 - (s2 - s1 * mu)) / m;
+        if (d < 0.0) break;
+        t = mu - sqrt(d);
       }
-      if (!(c > 0.0)) break;
-      bool ex;
-      const double tn = thr_step<NORM>(c, s1, s2, mn, mref, t, ex);
-      if (ex) return tn;
-      t = fmax(t, tn);
+      if (t < y) best = fmax(best, t);
     }
-    return t;
+    return mref + best;
   };
 
   // Raises the floors until every row has room for a full block in both of
@@ -837,7 +912,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     for (int it = 0; it < kRefloorSteps; ++it) {
       double c, s1, s2;
       float mn;
-      scan_buf<SCAP>(buf, cnt, floor_, (double)mrun, c, s1, s2, mn);
+      scan_buf<SCAP, CAP>(buf, cnt, floor_, (double)mrun, cz, c, s1, s2, mn);
       c += partner_d(c);
       s1 += partner_d(s1);
       s2 += partner_d(s2);
@@ -846,8 +921,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       if (!done_ && c > 0.0) {
         bool ex;
         const double tn = thr_step<NORM>(c, s1, s2, mn, (double)mrun, floor_, ex);
-        floor_ = fmax(floor_, tn);
-        floor_f = float_floor(floor_);
+        if (tn > floor_) set_floor(tn);
         done_ = fresh = ex;
         settled = settled || ex;
       } else {
@@ -909,10 +983,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       if (mt > mrun) {
         mrun = mt;
         const double fl = (double)mrun - 1.0;
-        if (fl > floor_) {
-          floor_ = fl;
-          floor_f = float_floor(floor_);
-        }
+        if (fl > floor_) set_floor(fl);
       }
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
@@ -924,53 +995,51 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
         if (__any(bz[kb] > floor_f && !ovf)) {
-          float z[16];
-          int na = 0;
+          float v[16];  // stored-domain values of the block
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            z[r] = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
-            na += z[r] > floor_f ? 1 : 0;
-          }
-          if (__any(!ovf && cnt + na > SCAP)) {
-            // a lane cannot take the block: raise the floors from the lists
-            // of block maxima and drop what fell below them ...
-            if (__any(dirty)) {
-              const double tf = top_floor();
-              if (!ovf && tf > floor_) {
-                floor_ = tf;
-                floor_f = float_floor(floor_);
-              }
-              dirty = false;
-            }
-            compact_buf<SCAP>(buf, cnt, floor_f);
-            na = 0;
+          for (int r = 0; r < 16; ++r) v[r] = CAP ? zval<true>(s[kb][r], cz, sc_over_cap, capz) : s[kb][r];
+          auto count = [&]() __attribute__((always_inline)) {
+            int n = 0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) na += z[r] > floor_f ? 1 : 0;
-            // ... and, if that is not enough, step the floors on the buffers
+            for (int r = 0; r < 16; ++r) n += v[r] > floor_v ? 1 : 0;
+            return n;
+          };
+          if (__any(!ovf && cnt + 16 > SCAP)) {
+            int na = count();
             if (__any(!ovf && cnt + na > SCAP)) {
-              refloor();
-              na = 0;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) na += z[r] > floor_f ? 1 : 0;
+              // a lane cannot take the block: raise the floors from the lists
+              // of block maxima and drop what fell below them ...
+              if (__any(dirty)) {
+                const double tf = top_floor();
+                if (!ovf && tf > floor_) set_floor(tf);
+                dirty = false;
+              }
+              compact_buf<SCAP>(buf, cnt, floor_v);
+              na = count();
+              // ... and, if that is not enough, step the floors on the buffers
+              if (__any(!ovf && cnt + na > SCAP)) {
+                refloor();
+                na = count();
+              }
             }
+            // a row whose lanes cannot take the block goes to the extra passes
+            const int full = (!ovf && cnt + na > SCAP) ? 1 : 0;
+            if (__any(full)) ovf = ovf || (full | partner_i(full)) != 0;
           }
-          // a row whose lanes cannot take the block goes to the extra passes
-          const int full = (!ovf && cnt + na > SCAP) ? 1 : 0;
-          if (__any(full)) ovf = ovf || (full | partner_i(full)) != 0;
-          if (!ovf && na > 0) {
+          if (!ovf) {
             if (cnt + 16 <= SCAP) {
               // branch-free: every value is written at the append position,
               // which only advances for the accepted ones
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                buf[cnt * 64] = z[r];
-                cnt += z[r] > floor_f ? 1 : 0;
+                buf[cnt * 64] = v[r];
+                cnt += v[r] > floor_v ? 1 : 0;
               }
             } else {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                if (z[r] > floor_f) {
-                  buf[cnt * 64] = z[r];
+                if (v[r] > floor_v) {
+                  buf[cnt * 64] = v[r];
                   ++cnt;
                 }
               }
@@ -984,6 +1053,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   wait_vmcnt<0>();
 
   // ---- exact threshold over the candidates ---------------------------------
+  // the lists of block maxima give a floor that often is tau itself (when the
+  // support is made of listed values), so most rows settle in one step
+  if (__any(dirty)) {
+    const double tf = top_floor();
+    if (!ovf && tf > floor_) set_floor(tf);
+  }
   double tau = INFINITY;
   int ksup = 0;
   bool done = !row_ok || mrun == -INFINITY || ovf;  // empty rows: tau = +inf, k = 0
@@ -992,7 +1067,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     if (!__any(!done)) break;
     double c, s1, s2;
     float mn;
-    scan_buf<SCAP>(buf, cnt, floor_, (double)mrun, c, s1, s2, mn);
+    scan_buf<SCAP, CAP>(buf, cnt, floor_, (double)mrun, cz, c, s1, s2, mn);
     c += partner_d(c);
     s1 += partner_d(s1);
     s2 += partner_d(s2);
@@ -1005,7 +1080,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         ksup = (int)c;
         done = true;
       } else {
-        floor_ = fmax(floor_, tn);
+        if (tn > floor_) set_floor(tn);
       }
     }
   }
@@ -1046,18 +1121,19 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         f32x16 s[C::NKB];
         qk_tile<C>(kl, qreg, l32, g, s);
         const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
-        float zz[C::NKB][16];
+        float vv[C::NKB][16];  // stored-domain values
         if (pending) {
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              float z = zval<CAP>(s[kb][r], cz, sc_over_cap, capz);
+              float v = CAP ? zval<true>(s[kb][r], cz, sc_over_cap, capz) : s[kb][r];
               if (edge) {
                 const int key = s_key(k0, kb, r, g);
-                if (key < mine.lo || key >= mine.hi) z = -INFINITY;
+                if (key < mine.lo || key >= mine.hi) v = -INFINITY;
               }
-              zz[kb][r] = z;
+              vv[kb][r] = v;
+              const float z = stored_z<CAP>(v, cz);
               if ((double)z > floor_) {
                 const double y = (double)z - mref;
                 c += 1.0;
@@ -1074,9 +1150,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                if ((double)zz[kb][r] > floor_) {
+                if (vv[kb][r] > floor_v) {
                   if (cnt < SCAP) {
-                    buf[cnt * 64] = zz[kb][r];
+                    buf[cnt * 64] = vv[kb][r];
                     ++cnt;
                   } else {
                     fits = 0;
@@ -1103,7 +1179,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         ksup = (int)c;
         pending = false;
       } else {
-        floor_ = fmax(floor_, tn);
+        if (tn > floor_) set_floor(tn);
       }
     }
     if (!pending) cnt = 0;
@@ -1112,7 +1188,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       if (!__any(solving)) break;
       double cc, a1, a2;
       float m1;
-      scan_buf<SCAP>(buf, cnt, floor_, mref, cc, a1, a2, m1);
+      scan_buf<SCAP, CAP>(buf, cnt, floor_, mref, cz, cc, a1, a2, m1);
       cc += partner_d(cc);
       a1 += partner_d(a1);
       a2 += partner_d(a2);
@@ -1126,7 +1202,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           solving = false;
           pending = false;
         } else {
-          floor_ = fmax(floor_, tn);
+          if (tn > floor_) set_floor(tn);
         }
       }
     }
@@ -1167,6 +1243,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       bool any = false;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
+        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
 #pragma clang fp contract(off)
@@ -1176,13 +1253,19 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             if (key < mine.lo || key >= mine.hi) z = -INFINITY;
           }
           const float d = z - tauf;
-          float p = d > 0.f ? d : 0.f;
-          if (ent) p = p * p;
-          any |= p > 0.f;
-          const bf16_t pb = (bf16_t)p;
-          wsum += (float)pb;
-          pk[2 * kb + (r >> 3)][r & 7] = pb;
+          p[r] = d > 0.f ? d : 0.f;
+          if (ent) p[r] = p[r] * p[r];
+          any |= p[r] > 0.f;
         }
+        pk[2 * kb] = p_operand(p);
+        pk[2 * kb + 1] = p_operand(p + 8);
+      }
+      // sum of the bf16-rounded weights (a bf16 is the high half of its float)
+#pragma unroll
+      for (int u = 0; u < 2 * C::NKB; ++u) {
+        const u32x4 w = __builtin_bit_cast(u32x4, pk[u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wsum += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
       }
       if (__any(any)) {
 #pragma unroll
