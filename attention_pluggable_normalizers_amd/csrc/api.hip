@@ -131,8 +131,8 @@ enum class Path { kNone, kGeneric, kPrefill, kDecode };
 
 Path select(const FwdArgs& a) {
   if ((int64_t)a.B * a.Hq * a.Lq == 0) return Path::kNone;
-  if (!a.paged && prefill_mfma_supported(a)) return Path::kPrefill;
   if (a.paged && decode_supported(a)) return Path::kDecode;
+  if (prefill_mfma_supported(a)) return Path::kPrefill;
   return Path::kGeneric;
 }
 

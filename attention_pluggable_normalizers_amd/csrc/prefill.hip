@@ -116,7 +116,15 @@ struct SeqSpan {
 };
 __device__ __forceinline__ SeqSpan seq_span(const FwdArgs& a, int b, int h) {
   SeqSpan s;
-  if (!a.cu_q) {
+  if (a.paged) {  // chunked prefill: Lq queries align bottom-right against the sequence's keys
+    s.Lq = a.Lq;
+    s.Lk = paged_live(a, b);
+    s.q_off = (int64_t)b * a.q_sb;
+    s.k_off = 0;  // pages are addressed through the block table
+    s.v_off = 0;
+    s.o_off = (int64_t)b * a.o_sb;
+    s.st_row = ((int64_t)b * a.Hq + h) * a.Lq;
+  } else if (!a.cu_q) {
     s.Lq = a.Lq;
     s.Lk = a.Lk;
     s.q_off = (int64_t)b * a.q_sb;
@@ -280,9 +288,27 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Paged K/V (chunked prefill through the block table).  One transfer covers
+// 64 / CPR consecutive keys, which lie in one page when the block size is a
+// multiple of 8 (checked on the host), so its page is wave-uniform: the
+// page's byte offset goes in the scalar offset, and the descriptor's record
+// count is cut at the sequence's last key, so the rows past it read as zeros
+// (their cache slots may hold anything, NaN included).
+struct PageCtx {
+  const int32_t* row;  // block-table row of the sequence; nullptr for contiguous K/V
+  int bs, max_blocks, nblk, Lk;
+  uint32_t kpage, vpage;  // page strides in bytes
+};
+
+__device__ __forceinline__ i32x4 with_records(i32x4 r, uint32_t n) {
+  r[2] = (int)n;
+  return r;
+}
+
 template <class C>
 struct DmaTiles {
   static constexpr int NI = C::KCH / 64 / C::NW;  // transfers per wave per K (and per V) tile
+  static constexpr int ROWS = 64 / C::CPR;        // tile rows one transfer covers
   static_assert(C::KCH % (64 * C::NW) == 0, "K/V tile must split into 1 KB transfers per wave");
   static constexpr int PER_TILE = 2 * NI;         // vmcnt events per tile
   uint32_t ko[NI], vo[NI];                        // per-lane byte offsets inside a tile
@@ -301,24 +327,79 @@ struct DmaTiles {
       vo[i] = row * vstr + (pc ^ v_swz<C>(row)) * 16;
     }
   }
-  __device__ __forceinline__ void issue_k(i32x4 rk, const bf16_t* kl, int k0, bool live) {
-    const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
+  // paged: byte offset of transfer i's first key and the records up to the
+  // sequence's last key (0 when none of its keys is live)
+  __device__ __forceinline__ void page_span(const PageCtx& pg, int key0, bool live, uint32_t kstride,
+                                            uint32_t page_bytes, uint32_t& soff, uint32_t& nrec) const {
+    const int valid = live ? min(max(pg.Lk - key0, 0), ROWS) : 0;
+    soff = 0;
+    nrec = 0;
+    if (valid > 0) {
+      // the table is read-only here: a constant-space read of a uniform index
+      // is a scalar load (no vector-memory count shared with the transfers)
+      const int idx = __builtin_amdgcn_readfirstlane(min(key0 / pg.bs, pg.max_blocks - 1));
+      const int raw = ((const __attribute__((address_space(4))) int32_t*)pg.row)[idx];
+      const int64_t page = min(max(raw, 0), pg.nblk - 1);
+      soff = (uint32_t)(page * page_bytes) + (uint32_t)(key0 % pg.bs) * kstride;
+      nrec = soff + (uint32_t)valid * kstride;
+    }
+    // wave-uniform by construction; made explicit for the scalar operands
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    nrec = __builtin_amdgcn_readfirstlane(nrec);
+  }
+  __device__ __forceinline__ void issue_k(i32x4 rk, const bf16_t* kl, int k0, bool live,
+                                          const PageCtx& pg) {
     const uint32_t kla = lds_addr(kl) + wave * 1024;
+    if (!pg.row) {
+      const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
+      for (int i = 0; i < NI; ++i) dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r0 = (i * C::NW + wave) * ROWS;
+        uint32_t ks, kn;
+        page_span(pg, k0 + r0, live, kstr, pg.kpage, ks, kn);
+        dma16(with_records(rk, kn), kla + i * C::NW * 1024, ko[i] - (uint32_t)r0 * kstr, ks);
+      }
+    }
   }
   __device__ __forceinline__ void issue(i32x4 rk, i32x4 rv, const bf16_t* kl, const bf16_t* vl, int k0,
-                                        bool live) {
-    const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
-    const uint32_t vs = live ? (uint32_t)k0 * vstr : 0x80000000u;
+                                        bool live, const PageCtx& pg) {
     const uint32_t kla = lds_addr(kl) + wave * 1024, vla = lds_addr(vl) + wave * 1024;
+    if (!pg.row) {
+      const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
+      const uint32_t vs = live ? (uint32_t)k0 * vstr : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
-      dma16(rv, vla + i * C::NW * 1024, vo[i], vs);
+      for (int i = 0; i < NI; ++i) {
+        dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
+        dma16(rv, vla + i * C::NW * 1024, vo[i], vs);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r0 = (i * C::NW + wave) * ROWS;
+        uint32_t ks, kn, vs, vn;
+        page_span(pg, k0 + r0, live, kstr, pg.kpage, ks, kn);
+        page_span(pg, k0 + r0, live, vstr, pg.vpage, vs, vn);
+        dma16(with_records(rk, kn), kla + i * C::NW * 1024, ko[i] - (uint32_t)r0 * kstr, ks);
+        dma16(with_records(rv, vn), vla + i * C::NW * 1024, vo[i] - (uint32_t)r0 * vstr, vs);
+      }
     }
   }
 };
+
+__device__ __forceinline__ PageCtx page_ctx(const FwdArgs& a, int b, int Lk) {
+  PageCtx pg;
+  pg.row = a.paged ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
+  pg.bs = a.block_size;
+  pg.max_blocks = a.max_blocks;
+  pg.nblk = a.num_blocks;
+  pg.Lk = Lk;
+  pg.kpage = (uint32_t)(a.k_sb * 2);
+  pg.vpage = (uint32_t)(a.v_sb * 2);
+  return pg;
+}
 
 // V^T operand (32 dims x 16 keys) of PV step t and dim block db, read from a
 // row-major V tile by two transposing LDS reads (ds_read_b64_tr_b16).  In each
@@ -490,13 +571,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 
   const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
   const i32x4 rv = rsrc_words(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
+  const PageCtx pg = page_ctx(a, b, Lk);
   DmaTiles<C> dma;
   dma.init(a.k_sl, a.v_sl, wave, lane);
   constexpr int kAhead = (NBUF - 2) * DmaTiles<C>::PER_TILE;  // transfers left in flight at a wait
 
   // tile t lives in stage (t - t0) % NBUF; stages of tiles t0 .. t0 + NBUF - 2 first
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) dma.issue(rk, rv, kl_of(u), vl_of(u), (t0 + u) * C::BN, t0 + u < t1);
+  for (int u = 0; u < NBUF - 1; ++u) dma.issue(rk, rv, kl_of(u), vl_of(u), (t0 + u) * C::BN, t0 + u < t1, pg);
   // everything, the Q loads included: the compiler then knows Q is in
   // registers and places no vmcnt wait inside the loop
   wait_vmcnt<0>();
@@ -506,7 +588,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
     // the stage of tile t + NBUF - 1 held tile t - 1, whose reads all ended
     // before the barrier that closed the previous step
     const int nxt = cur == 0 ? NBUF - 1 : cur - 1;
-    dma.issue(rk, rv, kl_of(nxt), vl_of(nxt), (t + NBUF - 1) * C::BN, t + NBUF - 1 < t1);
+    dma.issue(rk, rv, kl_of(nxt), vl_of(nxt), (t + NBUF - 1) * C::BN, t + NBUF - 1 < t1, pg);
     if (tile_active(t)) {
       f32x16 s[C::NKB];
       qk_tile<C>(kl_of(cur), qreg, l32, g, s);
@@ -935,6 +1017,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 
   const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
   const i32x4 rv = rsrc_words(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
+  const PageCtx pg = page_ctx(a, b, Lk);
   DmaTiles<C> dma;
   dma.init(a.k_sl, a.v_sl, wave, lane);
   constexpr int NA = SC::NA;
@@ -943,14 +1026,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // that the compiler needs no vmcnt wait inside the loops.
   auto k_prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NA - 1; ++u) dma.issue_k(rk, ka_of(u), (t0 + u) * C::BN, t0 + u < t1);
+    for (int u = 0; u < NA - 1; ++u) dma.issue_k(rk, ka_of(u), (t0 + u) * C::BN, t0 + u < t1, pg);
     wait_vmcnt<0>();
     lds_barrier();
   };
   // start of step t: K of tile t + NA - 1 into the stage tile t - 1 left
   auto k_next = [&](int t, int cur) __attribute__((always_inline)) {
     const int nxt = cur == 0 ? NA - 1 : cur - 1;
-    dma.issue_k(rk, ka_of(nxt), (t + NA - 1) * C::BN, t + NA - 1 < t1);
+    dma.issue_k(rk, ka_of(nxt), (t + NA - 1) * C::BN, t + NA - 1 < t1, pg);
   };
   // end of step t: this wave's part of tile t + 1 has landed, then the barrier
   auto k_done = [&](int& cur) __attribute__((always_inline)) {
@@ -1222,7 +1305,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   VTr<C> vtr;
   vtr.init(lane);
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) dma.issue(rk, rv, kb_of(u), vb_of(u), (t0 + u) * C::BN, t0 + u < t1);
+  for (int u = 0; u < NB - 1; ++u) dma.issue(rk, rv, kb_of(u), vb_of(u), (t0 + u) * C::BN, t0 + u < t1, pg);
   wait_vmcnt<0>();
   lds_barrier();
   cur = 0;
@@ -1231,7 +1314,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     const bf16_t* vl = vb_of(cur);
     {
       const int nxt = cur == 0 ? NB - 1 : cur - 1;
-      dma.issue(rk, rv, kb_of(nxt), vb_of(nxt), (t + NB - 1) * C::BN, t + NB - 1 < t1);
+      dma.issue(rk, rv, kb_of(nxt), vb_of(nxt), (t + NB - 1) * C::BN, t + NB - 1 < t1, pg);
     }
     const int k0 = t * C::BN;
     const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
@@ -1348,7 +1431,17 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 bool prefill_mfma_supported(const FwdArgs& a) {
-  if (a.dtype != ATTN_BF16 || a.paged) return false;
+  if (a.dtype != ATTN_BF16) return false;
+  if (a.paged) {
+    // chunked prefill: a transfer's keys must share a page, and every page
+    // offset must fit the 32-bit buffer offsets
+    if (a.Lq < 2 || a.block_size % 8 != 0) return false;
+    if ((int64_t)a.num_blocks * a.k_sb * 2 >= ((int64_t)1 << 32) ||
+        (int64_t)a.num_blocks * a.v_sb * 2 >= ((int64_t)1 << 32))
+      return false;
+    if (a.k_sl < a.D || a.v_sl < a.D) return false;
+    if ((int64_t)a.block_size * a.k_sl > a.k_sb || (int64_t)a.block_size * a.v_sl > a.v_sb) return false;
+  }
   if (a.D != 64 && a.D != 128 && a.D != 256) return false;
   if (!(a.scaling > 0.f)) return false;
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.out)) return false;
@@ -1357,7 +1450,8 @@ bool prefill_mfma_supported(const FwdArgs& a) {
   for (int64_t x : s)
     if (x % 8) return false;
   // K/V slices are addressed through 32-bit buffer records
-  if ((int64_t)a.Lk * a.k_sl * 2 >= ((int64_t)1 << 31) || (int64_t)a.Lk * a.v_sl * 2 >= ((int64_t)1 << 31))
+  if (!a.paged &&
+      ((int64_t)a.Lk * a.k_sl * 2 >= ((int64_t)1 << 31) || (int64_t)a.Lk * a.v_sl * 2 >= ((int64_t)1 << 31)))
     return false;
   const int nqb_min = (q_extent(a) + 127) / 128;
   return (int64_t)nqb_min * a.B * a.Hq <= (int64_t)INT32_MAX;

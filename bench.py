@@ -163,7 +163,7 @@ def extra_prefill(apn, W, dev, reps=10):
     return res
 
 
-def decode_bench(apn, W, dev, reps):
+def decode_bench(apn, W, dev, reps, chunk=0):
     import torch
     dcfg = W.DECODE
     x = W.make_paged(dcfg, device=dev)
@@ -186,12 +186,39 @@ def decode_bench(apn, W, dev, reps):
                    "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         del ws
     dom = max(dres, key=lambda n: dres[n]["us"])
-    return {"workload": dcfg.name, "B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv,
-            "head_dim": dcfg.D, "block_size": dcfg.block_size, "live_keys": int(sum(lens)),
-            "per_normalizer": dres,
-            "roofline": {"kernel": f"paged decode {dom}", "bound": "hbm",
-                         "achieved": dres[dom]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": dres[dom]["frac_hbm_peak"]}}
+    res = {"workload": dcfg.name, "B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv,
+           "head_dim": dcfg.D, "block_size": dcfg.block_size, "live_keys": int(sum(lens)),
+           "per_normalizer": dres,
+           "roofline": {"kernel": f"paged decode {dom}", "bound": "hbm",
+                        "achieved": dres[dom]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": dres[dom]["frac_hbm_peak"]}}
+    if chunk:
+        res["chunked_prefill"] = chunk_bench(apn, x, dcfg, lens, paged, dev, chunk)
+    return res
+
+
+def chunk_bench(apn, x, dcfg, lens, paged, dev, Lq, reps=5):
+    """Chunked prefill over the decode workload's paged cache: the last Lq
+    tokens of every sequence as queries (bottom-right causal against the
+    sequence's own length), on the matrix-core kernels through the block
+    table.  Credited FLOPs: 4 * D * unmasked pairs."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(dcfg.seed + 31)
+    q = torch.randn(dcfg.B, dcfg.Hq, Lq, dcfg.D, generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    st = torch.empty(*q.shape[:3], 2, dtype=torch.float32, device=dev)
+    pairs = sum(Lq * (n - Lq) + Lq * (Lq + 1) // 2 if n >= Lq else n * (n + 1) // 2 for n in lens)
+    flops = 4 * dcfg.D * pairs * dcfg.Hq
+    per = {}
+    for n in dcfg.normalizers:
+        f = lambda: apn.attn_fwd(q, x.k_cache, x.v_cache, out, st, normalizer=n, causal=True,
+                                 scaling=dcfg.scaling, paged=paged)
+        us = time_launches(f, reps, 2)
+        per[n] = {"us": round(us, 1), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                  "pct_bf16_peak": round(100 * flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del q, out, st
+    torch.cuda.empty_cache()
+    return {"Lq": Lq, "credited_flop_per_launch": flops, "per_normalizer": per}
 
 
 def main():
@@ -297,7 +324,8 @@ def main():
     if not args.no_extra:
         result["prefill_workloads"] = extra_prefill(apn, W, dev)
     if not args.no_decode:
-        result["decode"] = decode_bench(apn, W, dev, max(3, args.steps))
+        result["decode"] = decode_bench(apn, W, dev, max(3, args.steps),
+                                        chunk=0 if args.no_extra else 512)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)
