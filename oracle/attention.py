@@ -20,7 +20,7 @@ import math
 
 import numpy as np
 
-from .masks import allowed_mask
+from .masks import allowed_mask, block_mask_allowed
 from .normalizers import normalize_row, NORMALIZERS
 
 
@@ -49,13 +49,16 @@ def _check_params(normalizer, causal, window, softcap, scaling):
 
 def attention_forward(q, k, v, normalizer, causal=False, window=0, softcap=0.0,
                       scaling=None, seq_lens=None, rows=None, return_probs=False,
-                      row_block=512, sinks=None):
+                      row_block=512, sinks=None, block_mask=None):
     """Reference forward for q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
 
     ``seq_lens`` (optional, length B) limits the live keys of each batch entry
     (the paged path uses it; alignment stays bottom-right against it).
     ``sinks`` (optional, length Hq, softmax1 only): per query head, the logit
     of the virtual key in place of 0 (learned attention sinks).
+    ``block_mask`` (optional): ``(num_blocks [B,Hm,nqb], indices
+    [B,Hm,nqb,max], block_q, block_k)`` with Hm = 1 or Hq, a full-block CSR
+    key mask applied together with the causal / window / length rules.
     ``rows`` (optional) restricts the computation to a list of
     ``(b, h, i)`` query rows; then the result arrays hold only those rows, in
     that order: out [R, D], stats [R, 2].
@@ -77,12 +80,21 @@ def attention_forward(q, k, v, normalizer, causal=False, window=0, softcap=0.0,
     _check_params(normalizer, causal, window, softcap, scaling)
 
     masks = {}
+    if block_mask is not None:
+        bm_num, bm_idx, bm_bq, bm_bk = block_mask
+        bm_num = np.asarray(_as_f64(bm_num)).astype(np.int64)
+        bm_idx = np.asarray(_as_f64(bm_idx)).astype(np.int64)
 
-    def mask_for(b):
+    def mask_for(b, h=0):
         live = Lk if seq_lens is None else int(seq_lens[b])
-        if live not in masks:
-            masks[live] = allowed_mask(Lq, Lk, causal, window, seq_len=live)
-        return masks[live]
+        hm = 0 if block_mask is None or bm_num.shape[1] == 1 else h
+        key = (live, b, hm) if block_mask is not None else live
+        if key not in masks:
+            m = allowed_mask(Lq, Lk, causal, window, seq_len=live)
+            if block_mask is not None:
+                m = m & block_mask_allowed(Lq, Lk, bm_num[b, hm], bm_idx[b, hm], bm_bq, bm_bk)
+            masks[key] = m
+        return masks[key]
 
     def scores(b, h, i0, i1):
         kv = h // G
@@ -104,7 +116,7 @@ def attention_forward(q, k, v, normalizer, causal=False, window=0, softcap=0.0,
         details = []
         for r, (b, h, i) in enumerate(rows):
             s = scores(b, h, i, i + 1)[0]
-            idx, p, o, st = finish_row(b, h, s, mask_for(b)[i])
+            idx, p, o, st = finish_row(b, h, s, mask_for(b, h)[i])
             out[r] = o
             stats[r] = st
             if return_probs:
@@ -120,8 +132,8 @@ def attention_forward(q, k, v, normalizer, causal=False, window=0, softcap=0.0,
     stats = np.zeros((B, Hq, Lq, 2))
     probs = np.zeros((B, Hq, Lq, Lk)) if return_probs else None
     for b in range(B):
-        mask = mask_for(b)
         for h in range(Hq):
+            mask = mask_for(b, h)
             for i0 in range(0, Lq, row_block):
                 i1 = min(Lq, i0 + row_block)
                 s = scores(b, h, i0, i1)

@@ -11,10 +11,17 @@ Sources:
   i.e. the last query sees the last key.
 * "HF Attention Normalizers", "Differentiable Paged Attention": a paged
   sequence has ``sequence_lengths[b]`` live keys; later slots are never read.
+* "HF Attention Normalizers", "Important Limitations": explicit full-block
+  CSR masks (FlexAttention's ``BlockMask.from_kv_blocks`` with a no-op
+  mask_mod): per query block, a list of key blocks whose keys are all kept.
 
-Reading taken where the pages are silent: a window is only defined together
+Readings taken where the pages are silent: a window is only defined together
 with causal masking (the page defines it as causal AND distance < W), so a
-window without causal is rejected.
+window without causal is rejected.  A block mask restricts the keys further:
+a pair counts when its key block is listed AND the causal / window / length
+rules keep it.  List entries are taken in order; one outside the key-block
+range or not above its predecessor is ignored, and the count is clamped to
+the list length (FlexAttention's lists are ascending and in range).
 """
 
 import numpy as np
@@ -57,3 +64,25 @@ def kv_range(i, lq, live, causal, window=0):
     lo = 0 if not window else max(0, qp - window + 1)
     lo = min(lo, hi)
     return lo, hi
+
+
+def block_mask_allowed(lq, lk, num_blocks, indices, block_q, block_k):
+    """Boolean [lq, lk] of one (batch, head): key j is kept for query i iff
+    the key block j // block_k is a used entry of query block i // block_q's
+    list (``num_blocks[r]`` entries of ``indices[r]``)."""
+    if block_q <= 0 or block_k <= 0:
+        raise ValueError("block sizes must be > 0")
+    nkb = -(-lk // block_k)
+    nqb = -(-lq // block_q)
+    blocks = np.zeros((nqb, nkb), dtype=bool)
+    for r in range(nqb):
+        n = min(max(int(num_blocks[r]), 0), len(indices[r]))
+        prev = None
+        for e in range(n):
+            c = int(indices[r][e])
+            if 0 <= c < nkb and (prev is None or c > prev):
+                blocks[r, c] = True
+            prev = c
+    rows = np.arange(lq) // block_q
+    cols = np.arange(lk) // block_k
+    return blocks[rows][:, cols]
