@@ -45,10 +45,17 @@ class _Varlen(ctypes.Structure):
                 ("num_seqs", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32)]
 
 
+class _BlockMask(ctypes.Structure):
+    _fields_ = [("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("max_kv_blocks", ctypes.c_int32)]
+
+
 class _Params(ctypes.Structure):
     _fields_ = [("normalizer", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
-                ("scaling", ctypes.c_float), ("sinks", ctypes.c_void_p)]
+                ("scaling", ctypes.c_float), ("sinks", ctypes.c_void_p),
+                ("block_mask", ctypes.POINTER(_BlockMask))]
 
 
 _lib = None
@@ -111,7 +118,27 @@ def _desc(t):
     return d
 
 
-def _params(normalizer, causal, window, softcap, scaling, head_dim, sinks=None, num_heads=None):
+def _block_mask(block_mask):
+    """(kv_num_blocks int32 [B, Hm, nqb], kv_indices int32 [B, Hm, nqb, max], block_q,
+    block_k) -> the C descriptor (device tensors, contiguous)."""
+    num, idx, bq, bk = block_mask
+    for t, name, nd in ((num, "kv_num_blocks", 3), (idx, "kv_indices", 4)):
+        if (t.dtype != torch.int32 or t.dim() != nd or not t.is_contiguous()
+                or t.device.type != "cuda"):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor with {nd} dims")
+    if tuple(idx.shape[:3]) != tuple(num.shape):
+        raise ValueError("kv_indices must be [B, heads, q-blocks, max_kv_blocks] over kv_num_blocks")
+    m = _BlockMask()
+    m.kv_num_blocks = num.data_ptr()
+    m.kv_indices = idx.data_ptr()
+    m.block_q, m.block_k = int(bq), int(bk)
+    m.num_heads = int(num.shape[1])
+    m.max_kv_blocks = int(idx.shape[3])
+    return m
+
+
+def _params(normalizer, causal, window, softcap, scaling, head_dim, sinks=None, num_heads=None,
+            block_mask=None):
     p = _Params()
     p.normalizer = NORMALIZER_IDS.get(normalizer, -1) if isinstance(normalizer, str) else int(normalizer)
     p.causal = 1 if causal else 0
@@ -126,6 +153,9 @@ def _params(normalizer, causal, window, softcap, scaling, head_dim, sinks=None, 
         p.sinks = sinks.data_ptr()
     else:
         p.sinks = None
+    if block_mask is not None:
+        p._bm = _block_mask(block_mask)  # kept alive with the params
+        p.block_mask = ctypes.pointer(p._bm)
     return p
 
 
@@ -160,7 +190,8 @@ def attn_fwd_workspace_bytes(q, k, v, *, normalizer, causal=False, window=0, sof
 
 
 def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, window=0,
-             softcap=0.0, scaling=None, paged=None, workspace=None, stream=None, sinks=None):
+             softcap=0.0, scaling=None, paged=None, workspace=None, stream=None, sinks=None,
+             block_mask=None):
     """Enqueue the forward on ``stream`` (default: torch's current stream).
 
     q [B,Hq,Lq,D]; k, v [B,Hkv,Lk,D], or paged caches [NB,bs,Hkv,D] with
@@ -169,6 +200,9 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
     [B,Hq,Lq,2] or None) receive the results; returns ``(out, row_stats)``.
     ``sinks`` (softmax1 only): float32 device tensor [Hq] of learned sink
     logits, the virtual key's logit per query head (default 0).
+    ``block_mask``: ``(kv_num_blocks, kv_indices, block_q, block_k)``, a
+    full-block CSR key mask (int32 device tensors [B, 1 or Hq, q-blocks] and
+    [B, 1 or Hq, q-blocks, max_kv_blocks] with ascending block indices).
     """
     lib = load_library()
     if out is None:
@@ -177,7 +211,8 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
                                   or tuple(row_stats.shape) != (*q.shape[:3], 2)):
         raise ValueError("row_stats must be a contiguous float32 tensor [B, Hq, Lq, 2]")
     pd = _paged_desc(paged)
-    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
+                block_mask)
     if workspace is None:
         nbytes = attn_fwd_workspace_bytes(q, k, v, normalizer=normalizer, causal=causal,
                                           window=window, softcap=softcap, scaling=scaling,

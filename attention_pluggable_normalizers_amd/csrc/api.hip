@@ -124,6 +124,27 @@ int validate(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   a->norm = p->normalizer; a->causal = p->causal; a->window = p->window;
   a->softcap = p->softcap; a->scaling = p->scaling;
   a->sinks = p->sinks;
+  if (p->block_mask) {
+    const attn_block_mask* m = p->block_mask;
+    if (paged) return fail(ATTN_E_UNSUPPORTED, "block masks apply to contiguous K/V only");
+    if (m->block_q <= 0 || m->block_k <= 0) return fail(ATTN_E_INVALID, "block mask block sizes must be > 0");
+    if (m->num_heads != 1 && m->num_heads != Hq)
+      return fail(ATTN_E_INVALID, "block mask num_heads must be 1 or Hq");
+    if (m->max_kv_blocks < 0) return fail(ATTN_E_INVALID, "block mask max_kv_blocks must be >= 0");
+    if (!m->kv_num_blocks || (m->max_kv_blocks > 0 && !m->kv_indices))
+      return fail(ATTN_E_INVALID, "block mask kv_num_blocks or kv_indices is NULL");
+    if ((Lk + m->block_k - 1) / m->block_k > 16384)
+      return fail(ATTN_E_UNSUPPORTED, "block mask has more than 16384 key blocks");
+    const int64_t nqb = (Lq + m->block_q - 1) / m->block_q;
+    if (B * m->num_heads * nqb * (int64_t)m->max_kv_blocks > (int64_t)INT32_MAX * 8)
+      return fail(ATTN_E_UNSUPPORTED, "block mask too large");
+    a->bm_num = m->kv_num_blocks;
+    a->bm_idx = m->kv_indices;
+    a->bm_bq = m->block_q;
+    a->bm_bk = m->block_k;
+    a->bm_heads = m->num_heads;
+    a->bm_max = m->max_kv_blocks;
+  }
   return ATTN_OK;
 }
 
@@ -179,6 +200,7 @@ extern "C" int attn_fwd_varlen(const attn_tensor* q, const attn_tensor* k, const
   int st = validate(q, k, v, nullptr, p, out, row_stats, &a, true);
   if (st) return st;
   if (!varlen) return fail(ATTN_E_INVALID, "varlen descriptor is NULL");
+  if (a.bm_num) return fail(ATTN_E_UNSUPPORTED, "block masks apply to a padded batch only");
   if (q->shape[0] != 1 || k->shape[0] != 1)
     return fail(ATTN_E_INVALID, "packed q, k, v must have batch extent 1");
   if (varlen->num_seqs < 0 || varlen->max_seqlen_q < 0)

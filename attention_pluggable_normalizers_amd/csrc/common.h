@@ -38,7 +38,27 @@ struct FwdArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int max_q;
+  // block-sparse key mask (bm_num != nullptr): counts [B, bm_heads, nqb] and
+  // ascending key-block lists [B, bm_heads, nqb, bm_max], blocks bm_bq x bm_bk
+  const int32_t* bm_num;
+  const int32_t* bm_idx;
+  int bm_bq, bm_bk, bm_heads, bm_max;
 };
+
+// Key-block list of query block r of (b, h) under a block mask: entries e of
+// bm_idx + list_off(...), count clamped to [0, bm_max].
+__device__ __forceinline__ int64_t bm_list(const FwdArgs& a, int b, int h, int r, int& n) {
+  const int hm = a.bm_heads == 1 ? 0 : h;
+  const int nqb = (a.Lq + a.bm_bq - 1) / a.bm_bq;
+  const int64_t cell = ((int64_t)b * a.bm_heads + hm) * nqb + r;
+  n = min(max(a.bm_num[cell], 0), a.bm_max);
+  return cell * a.bm_max;
+}
+// Entry e of a list is used when it lies in [0, nkb) and above its predecessor.
+__device__ __forceinline__ bool bm_entry_ok(const int32_t* list, int e, int nkb) {
+  const int v = list[e];
+  return v >= 0 && v < nkb && (e == 0 || v > list[e - 1]);
+}
 
 // Query/key token ranges of packed request r, clamped into the packed arrays.
 __device__ __forceinline__ void varlen_ranges(const FwdArgs& a, int r, int& q0, int& q1, int& k0,

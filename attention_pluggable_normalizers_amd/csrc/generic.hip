@@ -28,6 +28,7 @@ namespace attn {
 namespace {
 
 constexpr int kMaxD = 256;
+constexpr int kMaxKeyBlocks = 16384;  // block masks: key blocks per row (bitmap in LDS)
 
 template <typename T>
 struct RowCtx {
@@ -71,6 +72,7 @@ template <typename T, int NORM>
 __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   __shared__ float qs[kMaxD];
   __shared__ float ps[64];
+  __shared__ unsigned kb_bits[kMaxKeyBlocks / 32];  // block mask: listed key blocks of this row
 
   const int64_t row = blockIdx.x;  // ((b * Hq) + h) * Lq + i; packed: h * Lq + token
   const int lane = threadIdx.x;
@@ -113,6 +115,24 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   int lo, hi;
   key_range(i, nq, live, a.causal, a.window, lo, hi);
 
+  // block mask: a bitmap of the key blocks listed for this row's query block
+  const bool bm = a.bm_num != nullptr;
+  if (bm) {
+    const int nkb = (live + a.bm_bk - 1) / a.bm_bk;
+    for (int w = lane; w < (nkb + 31) / 32; w += 64) kb_bits[w] = 0u;
+    __syncthreads();
+    int n;
+    const int32_t* list = a.bm_idx + bm_list(a, b, h, i / a.bm_bq, n);
+    for (int e = lane; e < n; e += 64)
+      if (bm_entry_ok(list, e, nkb)) atomicOr(&kb_bits[list[e] >> 5], 1u << (list[e] & 31));
+    __syncthreads();
+  }
+  auto allowed = [&](int j) -> bool {
+    if (!bm) return true;
+    const int c = j / a.bm_bk;
+    return (kb_bits[c >> 5] >> (c & 31)) & 1u;
+  };
+
   RowCtx<T> ctx(a, b, kvh, key0);
   const bool entmax = (NORM == ATTN_ENTMAX15);
   auto zval = [&](int j) -> float {
@@ -129,19 +149,27 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
 
   // softmax1: logit of the virtual key (0, or the head's learned sink)
   const float sink = (NORM == ATTN_SOFTMAX1 && a.sinks) ? a.sinks[h] : 0.f;
-  if (hi <= lo) {
+  auto write_empty = [&]() {  // a row without keys
     for (int d = lane; d < D; d += 64) orow[d] = from_f32<T>(0.f);
     if (srow && lane == 0) {
       srow[0] = NORM == ATTN_SOFTMAX ? -INFINITY : (NORM == ATTN_SOFTMAX1 ? sink : INFINITY);
       srow[1] = NORM == ATTN_SOFTMAX1 ? 1.f : 0.f;
     }
+  };
+  if (hi <= lo) {
+    write_empty();
     return;
   }
 
-  // pass 1: row max
+  // pass 1: row max (scores are finite, so -inf means no allowed key)
   float m = -INFINITY;
-  for (int j = lo + lane; j < hi; j += 64) m = fmaxf(m, zval(j));
+  for (int j = lo + lane; j < hi; j += 64)
+    if (allowed(j)) m = fmaxf(m, zval(j));
   m = wave_max(m);
+  if (m == -INFINITY) {
+    write_empty();
+    return;
+  }
 
   // Threshold search (sparse normalizers), in the shifted domain y = z - m.
   float tau_y = 0.f;
@@ -153,6 +181,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
       double s1 = 0.0, s2 = 0.0;
       float mn = INFINITY;
       for (int j = lo + lane; j < hi; j += 64) {
+        if (!allowed(j)) continue;
         const float y = zval(j) - m;
         if ((double)y > t) {
           cnt += 1;
@@ -202,7 +231,7 @@ __global__ __launch_bounds__(64) void generic_fwd_kernel(FwdArgs a) {
   for (int base = lo; base < hi; base += 64) {
     const int j = base + lane;
     float p = 0.f;
-    if (j < hi) {
+    if (j < hi && allowed(j)) {
       const float z = zval(j);
       if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1) {
         p = expf(z - mref);

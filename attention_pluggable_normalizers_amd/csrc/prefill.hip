@@ -389,6 +389,46 @@ struct DmaTiles {
   }
 };
 
+// Key tiles a workgroup visits, in order: the tiles [t0, t1) inside its
+// causal / window bounds, or, under a block mask, the tiles of its query
+// block's listed key blocks (sub tiles per block) that fall inside them.
+// tile(u) is the tile at position u, or -1 where there is nothing to do (an
+// entry the mask ignores, or a tile outside the bounds).  The lists are
+// read-only here: constant-space reads of uniform indices are scalar loads.
+struct TileSeq {
+  const __attribute__((address_space(4))) int32_t* list;  // nullptr: contiguous
+  int t0, t1, n, sub, nkb;
+  __device__ __forceinline__ int tile(int u) const {
+    if (!list) return t0 + u;
+    const int e = u / sub;
+    const int c = list[e];
+    const bool ok = c >= 0 && c < nkb && (e == 0 || c > list[e - 1]);
+    const int t = c * sub + (u - e * sub);
+    return (ok && t >= t0 && t < t1) ? t : -1;
+  }
+};
+
+template <class C>
+__device__ __forceinline__ TileSeq tile_seq(const FwdArgs& a, int b, int h, int qb, int t0, int t1,
+                                            int Lk) {
+  TileSeq ts;
+  ts.t0 = t0;
+  ts.t1 = t1;
+  ts.list = nullptr;
+  ts.n = t1 - t0;
+  ts.sub = 1;
+  ts.nkb = 0;
+  if (a.bm_num) {  // block_q == BM and block_k a multiple of BN (checked on the host)
+    int n;
+    const int64_t off = bm_list(a, b, h, qb, n);
+    ts.list = (const __attribute__((address_space(4))) int32_t*)(a.bm_idx + off);
+    ts.sub = a.bm_bk / C::BN;
+    ts.n = n * ts.sub;
+    ts.nkb = (Lk + a.bm_bk - 1) / a.bm_bk;
+  }
+  return ts;
+}
+
 __device__ __forceinline__ PageCtx page_ctx(const FwdArgs& a, int b, int Lk) {
   PageCtx pg;
   pg.row = a.paged ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
@@ -576,20 +616,27 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   dma.init(a.k_sl, a.v_sl, wave, lane);
   constexpr int kAhead = (NBUF - 2) * DmaTiles<C>::PER_TILE;  // transfers left in flight at a wait
 
-  // tile t lives in stage (t - t0) % NBUF; stages of tiles t0 .. t0 + NBUF - 2 first
+  const TileSeq ts = tile_seq<C>(a, b, h, qb, t0, t1, Lk);
+  auto tile_at = [&](int u) { return u < ts.n ? ts.tile(u) : -1; };
+  // position u of the sequence lives in stage u % NBUF; positions 0 .. NBUF - 2 first
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) dma.issue(rk, rv, kl_of(u), vl_of(u), (t0 + u) * C::BN, t0 + u < t1, pg);
+  for (int u = 0; u < NBUF - 1; ++u) {
+    const int tt = tile_at(u);
+    dma.issue(rk, rv, kl_of(u), vl_of(u), tt * C::BN, tt >= 0, pg);
+  }
   // everything, the Q loads included: the compiler then knows Q is in
   // registers and places no vmcnt wait inside the loop
   wait_vmcnt<0>();
   lds_barrier();
   int cur = 0;
-  for (int t = t0; t < t1; ++t) {
-    // the stage of tile t + NBUF - 1 held tile t - 1, whose reads all ended
-    // before the barrier that closed the previous step
+  for (int u = 0; u < ts.n; ++u) {
+    // the stage of position u + NBUF - 1 held position u - 1, whose reads all
+    // ended before the barrier that closed the previous step
     const int nxt = cur == 0 ? NBUF - 1 : cur - 1;
-    dma.issue(rk, rv, kl_of(nxt), vl_of(nxt), (t + NBUF - 1) * C::BN, t + NBUF - 1 < t1, pg);
-    if (tile_active(t)) {
+    const int tn = tile_at(u + NBUF - 1);
+    dma.issue(rk, rv, kl_of(nxt), vl_of(nxt), tn * C::BN, tn >= 0, pg);
+    const int t = ts.tile(u);
+    if (t >= 0 && tile_active(t)) {
       f32x16 s[C::NKB];
       qk_tile<C>(kl_of(cur), qreg, l32, g, s);
       consume(s, t, vl_of(cur));
@@ -849,7 +896,9 @@ __device__ __forceinline__ void compact_buf(float* buf, int& cnt, float t) {
   cnt = w;
 }
 
-template <class C, int NORM, bool CAP>
+// GEN: paged K/V or a block mask (tile sequence and page lookups); without
+// it both are compiled out of this register-heavy kernel.
+template <class C, int NORM, bool CAP, bool GEN>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_kernel(FwdArgs a) {
   using SC = SparseCfg<C>;
   constexpr int SCAP = SC::SCAP;
@@ -1017,23 +1066,34 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 
   const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
   const i32x4 rv = rsrc_words(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
-  const PageCtx pg = page_ctx(a, b, Lk);
+  PageCtx pg = page_ctx(a, b, Lk);
+  if (!GEN) pg.row = nullptr;
   DmaTiles<C> dma;
   dma.init(a.k_sl, a.v_sl, wave, lane);
   constexpr int NA = SC::NA;
   // K tiles t0 .. t0 + NA - 2 into stages 0 .. NA - 2; tile t sits in stage
   // (t - t0) mod NA.  Everything is waited for here, the Q loads included, so
   // that the compiler needs no vmcnt wait inside the loops.
+  TileSeq ts = tile_seq<C>(a, b, h, qb, t0, t1, Lk);
+  if (!GEN) {
+    ts.list = nullptr;
+    ts.n = t1 - t0;
+  }
+  auto tile_at = [&](int u) { return u < ts.n ? ts.tile(u) : -1; };
   auto k_prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NA - 1; ++u) dma.issue_k(rk, ka_of(u), (t0 + u) * C::BN, t0 + u < t1, pg);
+    for (int u = 0; u < NA - 1; ++u) {
+      const int tt = tile_at(u);
+      dma.issue_k(rk, ka_of(u), tt * C::BN, tt >= 0, pg);
+    }
     wait_vmcnt<0>();
     lds_barrier();
   };
-  // start of step t: K of tile t + NA - 1 into the stage tile t - 1 left
-  auto k_next = [&](int t, int cur) __attribute__((always_inline)) {
+  // start of step u: K of position u + NA - 1 into the stage position u - 1 left
+  auto k_next = [&](int u, int cur) __attribute__((always_inline)) {
     const int nxt = cur == 0 ? NA - 1 : cur - 1;
-    dma.issue_k(rk, ka_of(nxt), (t + NA - 1) * C::BN, t + NA - 1 < t1, pg);
+    const int tn = tile_at(u + NA - 1);
+    dma.issue_k(rk, ka_of(nxt), tn * C::BN, tn >= 0, pg);
   };
   // end of step t: this wave's part of tile t + 1 has landed, then the barrier
   auto k_done = [&](int& cur) __attribute__((always_inline)) {
@@ -1043,11 +1103,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   };
   k_prologue();
   int cur = 0;
-  for (int t = t0; t < t1; ++t) {
+  for (int u = 0; u < ts.n; ++u) {
     const bf16_t* kl = ka_of(cur);
-    k_next(t, cur);
+    k_next(u, cur);
+    const int t = ts.tile(u);
     const int k0 = t * C::BN;
-    const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+    const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
       f32x16 s[C::NKB];
       qk_tile<C>(kl, qreg, l32, g, s);
@@ -1195,11 +1256,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     int fits = pending ? 1 : 0;
     k_prologue();
     cur = 0;
-    for (int t = t0; t < t1; ++t) {
+    for (int u = 0; u < ts.n; ++u) {
       const bf16_t* kl = ka_of(cur);
-      k_next(t, cur);
+      k_next(u, cur);
+      const int t = ts.tile(u);
       const int k0 = t * C::BN;
-      const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(pending);
+      const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(pending);
       if (active) {
         f32x16 s[C::NKB];
         qk_tile<C>(kl, qreg, l32, g, s);
@@ -1305,19 +1367,24 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   VTr<C> vtr;
   vtr.init(lane);
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) dma.issue(rk, rv, kb_of(u), vb_of(u), (t0 + u) * C::BN, t0 + u < t1, pg);
+  for (int u = 0; u < NB - 1; ++u) {
+    const int tt = tile_at(u);
+    dma.issue(rk, rv, kb_of(u), vb_of(u), tt * C::BN, tt >= 0, pg);
+  }
   wait_vmcnt<0>();
   lds_barrier();
   cur = 0;
-  for (int t = t0; t < t1; ++t) {
+  for (int u = 0; u < ts.n; ++u) {
     const bf16_t* kl = kb_of(cur);
     const bf16_t* vl = vb_of(cur);
     {
       const int nxt = cur == 0 ? NB - 1 : cur - 1;
-      dma.issue(rk, rv, kb_of(nxt), vb_of(nxt), (t + NB - 1) * C::BN, t + NB - 1 < t1, pg);
+      const int tn = tile_at(u + NB - 1);
+      dma.issue(rk, rv, kb_of(nxt), vb_of(nxt), tn * C::BN, tn >= 0, pg);
     }
+    const int t = ts.tile(u);
     const int k0 = t * C::BN;
-    const bool active = wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+    const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
     if (active) {
       f32x16 s[C::NKB];
       qk_tile<C>(kl, qreg, l32, g, s);
@@ -1402,7 +1469,9 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
       kern<<<grid, block, lds, stream>>>(a);
       return hipGetLastError();
     };
-    return cap ? go(prefill_sparse_kernel<C, NORM, true>) : go(prefill_sparse_kernel<C, NORM, false>);
+    if (a.paged || a.bm_num)
+      return cap ? go(prefill_sparse_kernel<C, NORM, true, true>) : go(prefill_sparse_kernel<C, NORM, false, true>);
+    return cap ? go(prefill_sparse_kernel<C, NORM, true, false>) : go(prefill_sparse_kernel<C, NORM, false, false>);
   } else {
     if (cap)
       prefill_softmax_kernel<C, kStages<C>, NORM, true><<<grid, block, 0, stream>>>(a);
@@ -1432,6 +1501,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 bool prefill_mfma_supported(const FwdArgs& a) {
   if (a.dtype != ATTN_BF16) return false;
+  // block masks: one query block per workgroup, key blocks of whole tiles
+  if (a.bm_num && (a.bm_bq != 128 || a.bm_bk % 64 != 0)) return false;
   if (a.paged) {
     // chunked prefill: a transfer's keys must share a page, and every page
     // offset must fit the 32-bit buffer offsets

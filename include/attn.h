@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum attn_status {
@@ -94,6 +94,31 @@ typedef struct attn_paged_kv {
   int32_t max_blocks;          /* > 0; row length of block_table           */
 } attn_paged_kv;
 
+/* Block-sparse key mask in compressed-row form: FlexAttention's
+ * BlockMask.from_kv_blocks with a no-op mask_mod, i.e. explicit full-block
+ * CSR masks ("HF Attention Normalizers", "Important Limitations": such
+ * masks run without dense-mask expansion).  Query rows are grouped in
+ * blocks of block_q (row i in block i / block_q), keys in blocks of block_k;
+ * query block r of (b, h) may attend to the key blocks
+ * kv_indices[b, h', r, 0 .. kv_num_blocks[b, h', r] - 1] (h' = h, or 0 when
+ * num_heads == 1), every key of a listed block included.  Causal, window and
+ * live-length masking still apply on top.  Entries must be ascending; an
+ * entry outside [0, ceil(Lk / block_k)) or not above its predecessor is
+ * ignored, and counts are clamped to [0, max_kv_blocks].  Block indices
+ * count from key 0 and query 0 (top-left), independently of the
+ * bottom-right causal alignment.  Contiguous K/V only (no paged cache, no
+ * packed batch).  block_q == 128 with block_k a multiple of 64 runs on the
+ * matrix-core kernels (bf16, head dim 64/128/256); any other block shape on
+ * the per-row kernel (at most 16384 key blocks).                           */
+typedef struct attn_block_mask {
+  const int32_t* kv_num_blocks;  /* device int32 [B, num_heads, ceil(Lq / block_q)] */
+  const int32_t* kv_indices;     /* device int32 [B, num_heads, ceil(Lq / block_q), max_kv_blocks] */
+  int32_t block_q;               /* > 0 */
+  int32_t block_k;               /* > 0 */
+  int32_t num_heads;             /* 1 (shared by all query heads) or Hq */
+  int32_t max_kv_blocks;         /* >= 0 */
+} attn_block_mask;
+
 /* Forward parameters.
  *   causal  : keep key j for query i iff j <= i + (L - Lq), L the live key
  *             count (bottom-right alignment: "Packed Variable-Length
@@ -113,7 +138,9 @@ typedef struct attn_paged_kv {
  *             w_j = exp(s_j) / (exp(sinks[h]) + sum_k exp(s_k)).  The logit
  *             is used as given (no scaling, no softcap); values must be
  *             finite.  Any other normalizer with sinks != NULL is
- *             ATTN_E_INVALID.                                              */
+ *             ATTN_E_INVALID.
+ *   block_mask : NULL, or a host descriptor of a block-sparse key mask
+ *             (attn_block_mask; its arrays are on the device).            */
 typedef struct attn_params {
   int32_t normalizer;  /* attn_normalizer */
   int32_t causal;      /* 0 or 1 */
@@ -121,6 +148,7 @@ typedef struct attn_params {
   float softcap;
   float scaling;
   const float* sinks;  /* NULL or device float32 [Hq] (softmax1) */
+  const attn_block_mask* block_mask;  /* NULL or host descriptor */
 } attn_params;
 
 /* attn_fwd -- enqueue the forward on `stream` (a hipStream_t; NULL = the

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 3
+    assert apn.attn_abi_version() == 4
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -190,3 +190,37 @@ def test_varlen_validation(lib):
     vl.num_seqs, vl.cu_seqlens_k = 3, 0
     r, d = call(q, kv, ctypes.byref(vl))
     assert r == 1 and "NULL" in d
+
+
+def _bm(bq=128, bk=128, heads=1, maxb=4, num=0x7000, idx=0x8000):
+    m = B._BlockMask()
+    m.kv_num_blocks, m.kv_indices = num, idx
+    m.block_q, m.block_k, m.num_heads, m.max_kv_blocks = bq, bk, heads, maxb
+    return m
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(bq=0), 1, "block sizes"),
+    (dict(bk=-1), 1, "block sizes"),
+    (dict(heads=3), 1, "num_heads"),
+    (dict(maxb=-2), 1, "max_kv_blocks"),
+    (dict(num=0), 1, "NULL"),
+    (dict(idx=0), 1, "NULL"),
+    (dict(bk=1, maxb=1), 2, "16384"),  # 200000 keys in blocks of 1
+])
+def test_block_mask_validation(lib, kw, code, needle):
+    m = _bm(**kw)
+    p = _p()
+    p.block_mask = ctypes.pointer(m)
+    kv = _t((2, 2, 200000 if "16384" in needle else 64, 64))
+    r, d = _call(lib, _t(Q), kv, kv, p)
+    assert r == code and needle in d, d
+
+
+def test_block_mask_rejected_with_paged_cache(lib):
+    p = _p()
+    m = _bm()
+    p.block_mask = ctypes.pointer(m)
+    cache = _t((100, 16, 8, 128))
+    r, d = _call(lib, _t((4, 32, 3, 128)), cache, cache, p, paged=_paged())
+    assert r == 2 and "contiguous" in d
