@@ -38,6 +38,7 @@ from .normalizers import (
 )
 from .attention import (attention_forward, paged_attention_forward, gather_paged_kv,
                         varlen_attention_forward)
+from .backward import attention_backward
 
 __all__ = [
     "allowed_mask",
@@ -52,4 +53,5 @@ __all__ = [
     "paged_attention_forward",
     "gather_paged_kv",
     "varlen_attention_forward",
+    "attention_backward",
 ]
