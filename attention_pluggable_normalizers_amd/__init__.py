@@ -13,6 +13,7 @@ from .binding import (
     NORMALIZER_IDS,
     AttnError,
     attn_abi_version,
+    attn_bwd,
     attn_fwd,
     attn_fwd_varlen,
     attn_fwd_workspace_bytes,
@@ -31,6 +32,7 @@ __all__ = [
     "NORMALIZER_IDS",
     "AttnError",
     "attn_abi_version",
+    "attn_bwd",
     "attn_fwd",
     "attn_fwd_varlen",
     "attn_fwd_workspace_bytes",

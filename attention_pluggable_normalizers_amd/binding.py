@@ -83,6 +83,13 @@ def load_library(path=None):
     lib.attn_fwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged),
                                              P(_Params), P(ctypes.c_size_t)]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_void_p,
+                             P(_Params), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Params),
+                                             P(ctypes.c_size_t)]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_error_detail.argtypes = []
@@ -272,6 +279,36 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                              None, 0, stream)
     _check(st)
     return out, row_stats
+
+
+def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, softcap=0.0,
+             scaling=None, sinks=None, dq=None, dk=None, dv=None, sink_grad=False, stream=None):
+    """Gradients of ``attn_fwd`` for the same q, k, v and parameters, given the
+    forward's ``row_stats`` and the upstream gradient ``dout``: returns
+    ``(dq, dk, dv, dsinks)`` (``dsinks`` float32 [Hq] when ``sink_grad``,
+    softmax1 only, else None)."""
+    lib = load_library()
+    if (row_stats is None or row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+            or tuple(row_stats.shape) != (*q.shape[:3], 2)):
+        raise ValueError("row_stats must be the forward's float32 [B, Hq, Lq, 2]")
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    ds = torch.empty(q.shape[1], dtype=torch.float32, device=q.device) if sink_grad else None
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
+    qd, kd, vd = _desc(q), _desc(k), _desc(v)
+    n = ctypes.c_size_t(0)
+    _check(lib.attn_bwd_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                                        ctypes.byref(p), ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib.attn_bwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                        ctypes.byref(_desc(dout)), row_stats.data_ptr(), ctypes.byref(p),
+                        ctypes.byref(_desc(dq)), ctypes.byref(_desc(dk)), ctypes.byref(_desc(dv)),
+                        ds.data_ptr() if ds is not None else None, ws.data_ptr(), n.value,
+                        stream))
+    return dq, dk, dv, ds
 
 
 def custom_attention(module, query, key, value, attention_mask, *, normalizer, dropout=0.0,

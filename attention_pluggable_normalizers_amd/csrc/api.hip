@@ -162,6 +162,15 @@ size_t workspace_for(const FwdArgs& a) {
 }
 
 }  // namespace
+
+// For the backward entry points (backward.hip): the forward's validation of
+// q, k, v and the parameters (contiguous K/V), and the error-detail setter.
+int validate_fwd_args(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                      const attn_params* p, FwdArgs* a, bool need_data) {
+  return validate(q, k, v, nullptr, p, need_data ? q : nullptr, nullptr, a, need_data);
+}
+int bwd_fail(int status, const char* msg) { return fail(status, "%s", msg); }
+
 }  // namespace attn
 
 using namespace attn;

@@ -163,6 +163,26 @@ def extra_prefill(apn, W, dev, reps=10):
     return res
 
 
+def backward_bench(apn, cfg, q, k, v, norms, pairs, reps=3):
+    """Backward (attn_bwd) of the same workload from the forward's row
+    statistics: median time and TFLOP/s on the conventional 10 * D * pairs
+    (the five products of the backward: scores, dP, dV, dQ, dK)."""
+    import torch
+    g = torch.Generator(device=q.device).manual_seed(cfg.seed + 17)
+    do = torch.randn(q.shape, generator=g, device=q.device).to(q.dtype)
+    st = torch.empty(*q.shape[:3], 2, dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    flops = 10 * cfg.D * pairs
+    per = {}
+    for n in norms:
+        apn.attn_fwd(q, k, v, None, st, normalizer=n, causal=cfg.causal, scaling=cfg.scaling)
+        f = lambda: apn.attn_bwd(q, k, v, do, st, normalizer=n, causal=cfg.causal,
+                                 scaling=cfg.scaling, dq=dq, dk=dk, dv=dv)
+        us = time_launches(f, reps, 1)
+        per[n] = {"us": round(us, 1), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 2)}
+    return {"workload": cfg.name, "credited_flop_per_launch": flops, "per_normalizer": per}
+
+
 def decode_bench(apn, W, dev, reps, chunk=0):
     import torch
     dcfg = W.DECODE
@@ -319,6 +339,8 @@ def main():
         result["copy_calibration_bytes"] = n * 4
         del src, dst
 
+    if not args.no_extra:
+        result["backward"] = backward_bench(apn, cfg, q, k, v, norms, pairs)
     del q, k, v, out, stats
     torch.cuda.empty_cache()
     if not args.no_extra:

@@ -223,6 +223,33 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
                              const attn_tensor* v, const attn_paged_kv* paged,
                              const attn_params* p, size_t* bytes);
 
+/* attn_bwd -- gradients of attn_fwd ("HF Attention Normalizers",
+ * "Important Limitations": the fused backward recomputes the weights from
+ * the saved row statistics -- row max and denominator for softmax1, one
+ * threshold per row for the sparse normalizers).  For the same q, k, v and
+ * parameters as a forward that wrote `row_stats`, and the upstream gradient
+ * dout of its output:
+ *   dq   [B, Hq, Lq, D]  <- dL/dq
+ *   dk, dv [B, Hkv, Lk, D] <- dL/dk, dL/dv (summed over each key/value
+ *                            head's query heads)
+ *   dsinks : NULL, or (softmax1) device float32 [Hq] <- dL/d(sink logit)
+ *            (the logits are p->sinks, or 0 when that is NULL).
+ * dout, dq match q in shape and dtype; dk, dv match k, v; last dimension
+ * contiguous.  The sparse normalizers' gradients are the usual ones of the
+ * piecewise-smooth maps (sparsemax: dP minus its mean over the support, on
+ * the support; 1.5-entmax: sqrt(p) (dP - sum sqrt(p) dP / sum sqrt(p))).
+ * Contiguous K/V, no block mask.  fp32 arithmetic on the per-row kernels;
+ * every output is written in full.  workspace: attn_bwd_workspace_bytes
+ * (8 bytes per query row).  Errors as attn_fwd.                           */
+int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+             const attn_tensor* dout, const float* row_stats, const attn_params* p,
+             const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
+             float* dsinks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_bwd_workspace_bytes -- workspace size attn_bwd needs (host only). */
+int attn_bwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
+                             const attn_tensor* v, const attn_params* p, size_t* bytes);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_strerror(int status);
 

@@ -31,7 +31,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_varlen", "attn_fwd_workspace_bytes", "attn_strerror",
-                            "attn_last_error_detail", "attn_abi_version"])
+                            "attn_last_error_detail", "attn_abi_version", "attn_bwd",
+                            "attn_bwd_workspace_bytes"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -224,3 +225,29 @@ def test_block_mask_rejected_with_paged_cache(lib):
     cache = _t((100, 16, 8, 128))
     r, d = _call(lib, _t((4, 32, 3, 128)), cache, cache, p, paged=_paged())
     assert r == 2 and "contiguous" in d
+
+
+def test_backward_validation(lib):
+    q, kv = _t(Q), _t(KV)
+    n = ctypes.c_size_t(0)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv),
+                                        ctypes.byref(_p()), ctypes.byref(n)) == 0
+    assert n.value == 2 * 8 * 64 * 8
+
+    def call(dout=None, dq=None, dk=None, dv=None, stats=0x9000, p=None, dsinks=None, ws=0x9100,
+             wsn=1 << 20):
+        r = lib.attn_bwd(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv),
+                         ctypes.byref(dout or _t(Q)), stats, ctypes.byref(p or _p()),
+                         ctypes.byref(dq or _t(Q)), ctypes.byref(dk or _t(KV)),
+                         ctypes.byref(dv or _t(KV)), dsinks, ws, wsn, None)
+        return r, apn.attn_last_error_detail()
+    r, d = call(dq=_t((2, 8, 63, 64)))
+    assert r == 1 and "dq" in d
+    r, d = call(dk=_t(KV, torch.float32))
+    assert r == 1 and "dk" in d
+    r, d = call(stats=None)
+    assert r == 1 and "row_stats" in d
+    r, d = call(dsinks=0x9200)
+    assert r == 1 and "softmax1" in d
+    r, d = call(wsn=8)
+    assert r == 3 and "workspace" in d
