@@ -468,7 +468,8 @@ struct VTr {
   }
 };
 
-template <class C, int NBUF, int NORM, bool CAP>
+// GEN: paged K/V or a block mask (tile sequence and page lookups compiled in)
+template <class C, int NBUF, int NORM, bool CAP, bool GEN>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_kernel(FwdArgs a) {
   static_assert(NBUF == 2 || NBUF == 3, "two or three tiles in flight");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NBUF * 2 * C::BN * C::D];
@@ -611,12 +612,17 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 
   const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
   const i32x4 rv = rsrc_words(vbase, (uint32_t)((int64_t)Lk * a.v_sl * 2));
-  const PageCtx pg = page_ctx(a, b, Lk);
+  PageCtx pg = page_ctx(a, b, Lk);
+  if (!GEN) pg.row = nullptr;
   DmaTiles<C> dma;
   dma.init(a.k_sl, a.v_sl, wave, lane);
   constexpr int kAhead = (NBUF - 2) * DmaTiles<C>::PER_TILE;  // transfers left in flight at a wait
 
-  const TileSeq ts = tile_seq<C>(a, b, h, qb, t0, t1, Lk);
+  TileSeq ts = tile_seq<C>(a, b, h, qb, t0, t1, Lk);
+  if (!GEN) {
+    ts.list = nullptr;
+    ts.n = t1 - t0;
+  }
   auto tile_at = [&](int u) { return u < ts.n ? ts.tile(u) : -1; };
   // position u of the sequence lives in stage u % NBUF; positions 0 .. NBUF - 2 first
 #pragma unroll
@@ -638,7 +644,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
     const int t = ts.tile(u);
     if (t >= 0 && tile_active(t)) {
       f32x16 s[C::NKB];
+      __builtin_amdgcn_s_setprio(2);  // keep the matrix cores fed while others do VALU work
       qk_tile<C>(kl_of(cur), qreg, l32, g, s);
+      __builtin_amdgcn_s_setprio(0);
       consume(s, t, vl_of(cur));
     }
     wait_vmcnt<kAhead>();  // this wave's part of tile t + 1 has landed
@@ -1473,10 +1481,15 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
       return cap ? go(prefill_sparse_kernel<C, NORM, true, true>) : go(prefill_sparse_kernel<C, NORM, false, true>);
     return cap ? go(prefill_sparse_kernel<C, NORM, true, false>) : go(prefill_sparse_kernel<C, NORM, false, false>);
   } else {
-    if (cap)
-      prefill_softmax_kernel<C, kStages<C>, NORM, true><<<grid, block, 0, stream>>>(a);
+    const bool gen = a.paged || a.bm_num;
+    if (gen && cap)
+      prefill_softmax_kernel<C, kStages<C>, NORM, true, true><<<grid, block, 0, stream>>>(a);
+    else if (gen)
+      prefill_softmax_kernel<C, kStages<C>, NORM, false, true><<<grid, block, 0, stream>>>(a);
+    else if (cap)
+      prefill_softmax_kernel<C, kStages<C>, NORM, true, false><<<grid, block, 0, stream>>>(a);
     else
-      prefill_softmax_kernel<C, kStages<C>, NORM, false><<<grid, block, 0, stream>>>(a);
+      prefill_softmax_kernel<C, kStages<C>, NORM, false, false><<<grid, block, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
