@@ -710,20 +710,39 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 // ---------------------------------------------------------------------------
 
 // LDS of the sparse kernel (dynamic): NA K stages for the threshold passes,
-// then the candidate buffers; the output pass reuses all of it for NB K/V
-// stages.  Two workgroups per CU below D = 256 (their register use allows no
-// more), one at D = 256.
-template <class C>
+// then one candidate region per wave; the output pass either gathers V rows
+// through the buffers or reuses all of the LDS for NB K/V stages.  Two
+// workgroups per CU below D = 256 (their register use allows no more), one
+// at D = 256.
+//
+// A wave's region holds, per lane, entry e at byte 256 e + 4 lane: the float
+// value.  While the wave is "keyed" its entries stop at SCAP_K and each has a
+// 16-bit key index at KEYS_OFF + 128 e + 2 lane; a wave whose candidates
+// outgrow that drops the keys and uses the whole region for SCAP_F values
+// (the first SCAP_K values stay where they are).
+//
+// Only sparsemax keeps keys (KEYS): its candidates above the first floor
+// (row max - 1) are few, so the buffers hold their support with room to
+// spare, and it takes two K stages to leave more room.  1.5-entmax's first
+// floor (z max - 1, i.e. two score units) admits several times its support;
+// with keys its buffers overflow into extra compaction that costs more than
+// the gather saves, and its extra passes gain from a third K stage.
+template <class C, int NORM>
 struct SparseCfg {
+  static constexpr bool KEYS = NORM == ATTN_SPARSEMAX;
   static constexpr int LDS_BYTES = C::D == 256 ? 160 * 1024 : 80 * 1024;
-  static constexpr int NA = 3;                     // K tiles in flight, threshold passes
+  static constexpr int NA = KEYS ? 2 : 3;          // K tiles in flight, threshold passes
   static constexpr int NB = 3;                     // K/V tiles in flight, output pass
   static constexpr int KTILE = C::BN * C::D * 2;   // bytes of one K (or V) tile
-  static constexpr int REGION_BYTES = LDS_BYTES - NA * KTILE;  // candidate buffers
-  static constexpr int SCAP = REGION_BYTES / (C::NT * 4) / 8 * 8;  // candidates per lane
+  static constexpr int WREG = (LDS_BYTES - NA * KTILE) / C::NW / 256 * 256;  // bytes per wave
+  static constexpr int SCAP_F = WREG / 256 / 8 * 8;        // values per lane, no keys
+  static constexpr int SCAP_K = WREG / 384 / 8 * 8;        // values per lane with keys
+  static constexpr int KEYS_OFF = SCAP_K * 256;            // key indices, from the region start
   static_assert(NB * 2 * KTILE <= LDS_BYTES, "output pass stages must fit");
-  static_assert(SCAP >= 32, "candidate buffer too small");
+  static_assert(SCAP_K >= 32 && KEYS_OFF + SCAP_K * 128 <= WREG && SCAP_F >= 32, "candidate buffer too small");
 };
+
+typedef unsigned short u16;
 
 __device__ __forceinline__ float max16(const f32x16& v) {
   float m = v[0];
@@ -852,26 +871,29 @@ __device__ __forceinline__ float stored_z(float v, float cz) {
 
 // Keeps this lane's candidates with z above t (compacting them) and returns
 // their partial sums of y = z - mref.  Entries are read 8 at a time so their
-// LDS latencies overlap (SCAP is a multiple of 8, so the reads stay inside
-// the lane's buffer); compaction only writes to slots already read.
-template <int SCAP, bool CAP>
-__device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double mref, float cz,
+// LDS latencies overlap (the capacities are multiples of 8, so the reads stay
+// inside the lane's buffer); compaction only writes to slots already read.
+// KEYED: the key indices move with their values.
+template <bool CAP, bool KEYED>
+__device__ __forceinline__ void scan_buf(float* buf, u16* kbuf, int& cnt, double t, double mref, float cz,
                                          double& c, double& s1, double& s2, float& mn) {
-  static_assert(SCAP % 8 == 0, "buffer length must be a multiple of 8");
   int w = 0;
   c = s1 = s2 = 0.0;
   mn = INFINITY;
   for (int e0 = 0; e0 < cnt; e0 += 8) {
     float v[8], z[8];
+    u16 key[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       v[j] = buf[(e0 + j) * 64];
+      if (KEYED) key[j] = kbuf[(e0 + j) * 64];
       z[j] = stored_z<CAP>(v[j], cz);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (e0 + j < cnt && (double)z[j] > t) {
         buf[w * 64] = v[j];
+        if (KEYED) kbuf[w * 64] = key[j];
         ++w;
         const double y = (double)z[j] - mref;
         c += 1.0;
@@ -886,17 +908,22 @@ __device__ __forceinline__ void scan_buf(float* buf, int& cnt, double t, double 
 
 // Keeps this lane's candidates above t, a threshold in the stored domain
 // (compacting them in place).
-template <int SCAP>
-__device__ __forceinline__ void compact_buf(float* buf, int& cnt, float t) {
+template <bool KEYED>
+__device__ __forceinline__ void compact_buf(float* buf, u16* kbuf, int& cnt, float t) {
   int w = 0;
   for (int e0 = 0; e0 < cnt; e0 += 8) {
     float z[8];
+    u16 key[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) z[j] = buf[(e0 + j) * 64];
+    for (int j = 0; j < 8; ++j) {
+      z[j] = buf[(e0 + j) * 64];
+      if (KEYED) key[j] = kbuf[(e0 + j) * 64];
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (e0 + j < cnt && z[j] > t) {
         buf[w * 64] = z[j];
+        if (KEYED) kbuf[w * 64] = key[j];
         ++w;
       }
     }
@@ -904,12 +931,89 @@ __device__ __forceinline__ void compact_buf(float* buf, int& cnt, float t) {
   cnt = w;
 }
 
+// Output of a row whose support is the contents of its two lanes' candidate
+// buffers (value and key index per entry): both lanes walk the same entries,
+// lane l32's first, then lane l32 + 32's, and each accumulates
+// g(z - tau) * v over its half of the head dimension in fp32 (V rows are read
+// through the key indices, and for a paged cache through the block table; no
+// score is recomputed).  The weights sum to one up to rounding; the output
+// is divided by their fp32 sum.
+template <class C, int NORM, bool CAP>
+__device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, int cnt, int g, float tauf,
+                                            float cz, const bf16_t* vbase, int64_t v_sl, int64_t v_sb,
+                                            const PageCtx& pg, bf16_t* orow, bool row_ok) {
+  constexpr int DH = C::D / 2;                  // dims of this lane
+  constexpr int NV = DH / 8;                    // 16-byte pieces of its half row
+  constexpr int U = C::D == 64 ? 4 : (C::D == 128 ? 2 : 1);  // entries in flight
+  const int pc = partner_i(cnt);
+  const int n0 = g ? pc : cnt;                  // entries of lane l32
+  const int n = cnt + pc;
+  const int lead = g ? -32 : 0;                 // lane l32's slot relative to this lane
+  const bf16_t* const vcol = vbase + g * DH;
+  float acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+  float wsum = 0.f;
+  for (int e = 0; __any(e < n); e += U) {
+    float p[U];
+    u32x4 w[U][NV];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int i = e + j;
+      const bool ok = i < n;
+      // past the end: weight 0 and key 0 (a row of this sequence whenever
+      // any lane of the wave has entries)
+      const int slot = !ok ? 0 : (i < n0 ? lead + i * 64 : lead + 32 + (i - n0) * 64);
+      const float v = buf[slot];
+      const int key = ok ? (int)kbuf[slot] : 0;
+      float pw;
+      {
+#pragma clang fp contract(off)
+        const float d = stored_z<CAP>(v, cz) - tauf;
+        pw = d > 0.f ? d : 0.f;
+        if (NORM == ATTN_ENTMAX15) pw = pw * pw;
+      }
+      p[j] = ok ? pw : 0.f;
+      int64_t off;
+      if (pg.row) {
+        const int64_t page = page_of(pg.row, min(key / pg.bs, pg.max_blocks - 1), pg.nblk);
+        off = page * v_sb + (int64_t)(key % pg.bs) * v_sl;
+      } else {
+        off = (int64_t)key * v_sl;
+      }
+      const u32x4* vr = (const u32x4*)(vcol + off);
+#pragma unroll
+      for (int c = 0; c < NV; ++c) w[j][c] = vr[c];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      wsum += p[j];
+#pragma unroll
+      for (int c = 0; c < NV; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[8 * c + 2 * q] += p[j] * __uint_as_float(w[j][c][q] << 16);
+          acc[8 * c + 2 * q + 1] += p[j] * __uint_as_float(w[j][c][q] & 0xffff0000u);
+        }
+    }
+  }
+  if (row_ok) {
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      bf16x8 o;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = (bf16_t)(acc[8 * c + q] * inv);
+      *(bf16x8*)(orow + g * DH + 8 * c) = o;
+    }
+  }
+}
+
 // GEN: paged K/V or a block mask (tile sequence and page lookups); without
 // it both are compiled out of this register-heavy kernel.
 template <class C, int NORM, bool CAP, bool GEN>
 __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_kernel(FwdArgs a) {
-  using SC = SparseCfg<C>;
-  constexpr int SCAP = SC::SCAP;
+  using SC = SparseCfg<C, NORM>;
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];  // SC::LDS_BYTES
   constexpr int KT = C::BN * C::D;  // elements of one K or V tile
   auto ka_of = [&](int u) { return lds + u * KT; };  // threshold passes: K stage u
@@ -962,7 +1066,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   const float capz = CAP ? (ent ? 0.5f * a.softcap : a.softcap) : 0.f;
 
   // ---- pass A: row max, floor and candidates --------------------------------
-  float* const buf = (float*)(lds + SC::NA * KT) + wave * SCAP * 64 + lane;
+  char* const region = (char*)(lds + SC::NA * KT) + wave * SC::WREG;
+  float* const buf = (float*)region + lane;
+  u16* const kbuf = (u16*)(region + SC::KEYS_OFF) + lane;
   float mrun = -INFINITY;     // running max of z over the row (both lanes)
   double floor_ = -INFINITY;  // lower bound on tau (z units)
   float floor_f = -INFINITY;  // largest float <= floor_
@@ -973,6 +1079,15 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     floor_v = CAP ? floor_f : raw_floor(floor_f, cz);
   };
   int cnt = 0;                // this lane's candidates
+  bool keyed = SC::KEYS;     // wave-uniform: the buffers carry key indices
+  int cap = SC::KEYS ? SC::SCAP_K : SC::SCAP_F;  // wave-uniform: entries per lane
+  auto scan = [&](double t, double mref, double& c, double& s1, double& s2, float& mn)
+                  __attribute__((always_inline)) {
+    if (SC::KEYS && keyed)
+      scan_buf<CAP, true>(buf, kbuf, cnt, t, mref, cz, c, s1, s2, mn);
+    else
+      scan_buf<CAP, false>(buf, kbuf, cnt, t, mref, cz, c, s1, s2, mn);
+  };
   bool ovf = !row_ok;         // row left to the extra passes (or no row at all)
   bool settled = false;       // floor has reached the exact threshold of the keys seen once
 
@@ -1051,7 +1166,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     for (int it = 0; it < kRefloorSteps; ++it) {
       double c, s1, s2;
       float mn;
-      scan_buf<SCAP, CAP>(buf, cnt, floor_, (double)mrun, cz, c, s1, s2, mn);
+      scan(floor_, (double)mrun, c, s1, s2, mn);
       c += partner_d(c);
       s1 += partner_d(s1);
       s2 += partner_d(s2);
@@ -1067,7 +1182,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         done_ = true;
       }
       const int pc = partner_i(cnt);
-      const bool need = (cnt + 16 > SCAP || pc + 16 > SCAP) && (!done_ || fresh);
+      const bool need = (cnt + 16 > cap || pc + 16 > cap) && (!done_ || fresh);
       if (!__any(need)) break;
     }
   };
@@ -1156,9 +1271,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             for (int r = 0; r < 16; ++r) n += v[r] > floor_v ? 1 : 0;
             return n;
           };
-          if (__any(!ovf && cnt + 16 > SCAP)) {
+          if (__any(!ovf && cnt + 16 > cap)) {
             int na = count();
-            if (__any(!ovf && cnt + na > SCAP)) {
+            if (__any(!ovf && cnt + na > cap)) {
               // a lane cannot take the block: raise the floors from the lists
               // of block maxima and drop what fell below them ...
               if (__any(dirty)) {
@@ -1166,32 +1281,51 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
                 if (!ovf && tf > floor_) set_floor(tf);
                 dirty = false;
               }
-              compact_buf<SCAP>(buf, cnt, floor_v);
+              if (SC::KEYS && keyed)
+                compact_buf<true>(buf, kbuf, cnt, floor_v);
+              else
+                compact_buf<false>(buf, kbuf, cnt, floor_v);
               na = count();
               // ... and, if that is not enough, step the floors on the buffers
-              if (__any(!ovf && cnt + na > SCAP)) {
+              if (__any(!ovf && cnt + na > cap)) {
                 refloor();
                 na = count();
               }
+              // ... and, still short, give up the key indices for room
+              if (SC::KEYS && keyed && __any(!ovf && cnt + na > cap)) {
+                keyed = false;
+                cap = SC::SCAP_F;
+              }
             }
             // a row whose lanes cannot take the block goes to the extra passes
-            const int full = (!ovf && cnt + na > SCAP) ? 1 : 0;
+            const int full = (!ovf && cnt + na > cap) ? 1 : 0;
             if (__any(full)) ovf = ovf || (full | partner_i(full)) != 0;
           }
           if (!ovf) {
-            if (cnt + 16 <= SCAP) {
+            const int kk = s_key(k0, kb, 0, g);  // key of value 0; value r adds s_key(0, 0, r, 0)
+            if (cnt + 16 <= cap) {
               // branch-free: every value is written at the append position,
               // which only advances for the accepted ones
+              if (SC::KEYS && keyed) {
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                buf[cnt * 64] = v[r];
-                cnt += v[r] > floor_v ? 1 : 0;
+                for (int r = 0; r < 16; ++r) {
+                  buf[cnt * 64] = v[r];
+                  kbuf[cnt * 64] = (u16)(kk + s_key(0, 0, r, 0));
+                  cnt += v[r] > floor_v ? 1 : 0;
+                }
+              } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  buf[cnt * 64] = v[r];
+                  cnt += v[r] > floor_v ? 1 : 0;
+                }
               }
             } else {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 if (v[r] > floor_v) {
                   buf[cnt * 64] = v[r];
+                  if (SC::KEYS && keyed) kbuf[cnt * 64] = (u16)(kk + s_key(0, 0, r, 0));
                   ++cnt;
                 }
               }
@@ -1215,11 +1349,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   int ksup = 0;
   bool done = !row_ok || mrun == -INFINITY || ovf;  // empty rows: tau = +inf, k = 0
   bool pending = row_ok && mrun != -INFINITY && ovf;  // left to the extra passes
-  for (int it = 0; it < 2 * SCAP + 4; ++it) {
+  // the row's support is exactly the contents of its two lanes' buffers
+  // (an empty row's are empty); false for a row solved from running totals
+  bool inbuf = !ovf;
+  for (int it = 0; it < 2 * SC::SCAP_F + 4; ++it) {
     if (!__any(!done)) break;
     double c, s1, s2;
     float mn;
-    scan_buf<SCAP, CAP>(buf, cnt, floor_, (double)mrun, cz, c, s1, s2, mn);
+    scan(floor_, (double)mrun, c, s1, s2, mn);
     c += partner_d(c);
     s1 += partner_d(s1);
     s2 += partner_d(s2);
@@ -1236,7 +1373,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       }
     }
   }
-  if (!done) pending = true;  // cannot happen (each step drops a candidate); kept as a guard
+  if (!done) {  // cannot happen (each step drops a candidate); kept as a guard
+    pending = true;
+    inbuf = false;
+  }
 
   // ---- extra passes for rows whose candidates outgrew the buffer -----------
   // Each pass re-streams the K tiles and, for every pending row, both
@@ -1260,7 +1400,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     double c = 0.0, s1 = 0.0, s2 = 0.0;
     float mn = INFINITY;
     const double mref = (double)mrun;
-    cnt = 0;
+    if (pending) cnt = 0;  // solved rows keep their support
     int fits = pending ? 1 : 0;
     k_prologue();
     cur = 0;
@@ -1304,8 +1444,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 if (vv[kb][r] > floor_v) {
-                  if (cnt < SCAP) {
+                  if (cnt < cap) {
                     buf[cnt * 64] = vv[kb][r];
+                    if (SC::KEYS && keyed) kbuf[cnt * 64] = (u16)s_key(k0, kb, r, g);
                     ++cnt;
                   } else {
                     fits = 0;
@@ -1331,17 +1472,17 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         tau = tn;
         ksup = (int)c;
         pending = false;
+        cnt = 0;
       } else {
         if (tn > floor_) set_floor(tn);
       }
     }
-    if (!pending) cnt = 0;
     bool solving = pending && fits;
-    for (int it = 0; it < 2 * SCAP + 4; ++it) {
+    for (int it = 0; it < 2 * SC::SCAP_F + 4; ++it) {
       if (!__any(solving)) break;
       double cc, a1, a2;
       float m1;
-      scan_buf<SCAP, CAP>(buf, cnt, floor_, mref, cz, cc, a1, a2, m1);
+      scan(floor_, mref, cc, a1, a2, m1);
       cc += partner_d(cc);
       a1 += partner_d(a1);
       a2 += partner_d(a2);
@@ -1354,6 +1495,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           ksup = (int)cc;
           solving = false;
           pending = false;
+          inbuf = true;
         } else {
           if (tn > floor_) set_floor(tn);
         }
@@ -1363,6 +1505,20 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 
   // ---- pass B: weighted sum of V ------------------------------------------------
   const float tauf = (float)tau;
+  bf16_t* const orow = (bf16_t*)a.out + sp.o_off + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
+  if (row_ok && a.stats && g == 0) {
+    float* st = a.stats + (sp.st_row + myq) * 2;
+    st[0] = (float)tau;
+    st[1] = (float)ksup;
+  }
+  // When the support of every row of the workgroup sits in the buffers (and
+  // the keys fit their 16-bit indices), the output gathers the V rows of the
+  // support; otherwise the scores are recomputed tile by tile and the
+  // weighted sum runs on the matrix cores.
+  if (SC::KEYS && Lk <= 65536 && !block_any(!keyed || (row_ok && !inbuf))) {
+    gather_rows<C, NORM, CAP>(buf, kbuf, cnt, g, tauf, cz, vbase, a.v_sl, a.v_sb, pg, orow, row_ok);
+    return;
+  }
   // the weights sum to one; the output is divided by the sum of their
   // bf16-rounded values, which cancels most of the rounding of P
   float wsum = 0.f;
@@ -1441,7 +1597,6 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   const float wtot = wsum + partner(wsum);
   if (row_ok) {
     const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
-    bf16_t* orow = (bf16_t*)a.out + sp.o_off + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
@@ -1451,11 +1606,6 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(o[db][4 * rq + e] * inv);
         *(bf16x4*)(orow + db * 32 + 8 * rq + 4 * g) = w;
       }
-    }
-    if (a.stats && g == 0) {
-      float* st = a.stats + (sp.st_row + myq) * 2;
-      st[0] = (float)tau;
-      st[1] = (float)ksup;
     }
   }
 }
@@ -1470,7 +1620,7 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(nqb * a.B * a.Hq)), block(C::NT);
   const bool cap = a.softcap > 0.f;
   if constexpr (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
-    constexpr int lds = SparseCfg<C>::LDS_BYTES;
+    constexpr int lds = SparseCfg<C, NORM>::LDS_BYTES;
     auto go = [&](auto kern) {
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;

@@ -96,3 +96,22 @@ def test_qwen_full_size(norm, sigma):
     _, st = _full_size(W.qwen(sigma), norm, n_random=12)
     if norm != "softmax1":
         print(f"qwen sigma={sigma} {norm}: mean support {st[..., 1].mean():.2f}")
+
+
+@pytest.mark.parametrize("lk", [65536, 65600])
+@pytest.mark.parametrize("norm", ("sparsemax", "entmax15"))
+def test_sparse_long_key_range(norm, lk):
+    # the sparse output pass gathers V rows through 16-bit key indices when
+    # every key index fits them (lk <= 65536) and recomputes the scores tile
+    # by tile otherwise; both sides of that boundary, keys near the far end
+    # included (non-causal rows see every key; the last query rows are checked)
+    lq = 40
+    q = _rand((1, 2, lq, 64), 60, 2.0)
+    k = _rand((1, 1, lk, 64), 61, 2.0)
+    v = _rand((1, 1, lk, 64), 62)
+    # make the last keys win for some rows: copy query rows into the far end
+    k[0, 0, lk - 8:] = q[0, 0, :8] * 1.5
+    out, st = gpu_fwd(q, k, v, norm, False, 0, 0.0, 0.125)
+    rows = [(0, h, i) for h in range(2) for i in (0, 3, 7, 8, 20, lq - 1)]
+    check_rows(out, st, rows, q, k, v, norm, False, 0, 0.0, 0.125, where=f"lk{lk}")
+    assert (st[0, 0, :8, 1] >= 1).all()
