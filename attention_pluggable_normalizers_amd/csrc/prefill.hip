@@ -721,25 +721,37 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 // outgrow that drops the keys and uses the whole region for SCAP_F values
 // (the first SCAP_K values stay where they are).
 //
-// Only sparsemax keeps keys (KEYS): its candidates above the first floor
-// (row max - 1) are few, so the buffers hold their support with room to
-// spare, and it takes two K stages to leave more room.  1.5-entmax's first
-// floor (z max - 1, i.e. two score units) admits several times its support;
-// with keys its buffers overflow into extra compaction that costs more than
-// the gather saves, and its extra passes gain from a third K stage.
+// Key indices (KEYS) are kept, with two K stages in pass A to leave room for
+// them, for sparsemax and for 1.5-entmax at D >= 128.  At D = 64 entmax's
+// first floor (z max - 1, i.e. two score units) admits several times its
+// support, and with keys its buffers overflow into compaction that costs
+// more than the gather saves; it keeps three stages and values only.
+// The extra passes always stream K through NX = 3 stages: once a row is in
+// them its wave has dropped the keys (the output runs on the matrix cores),
+// so the candidate regions move behind the third stage (WREG_X, SCAP_X).
+template <int N>
+struct Stages {
+  static constexpr int value = N;
+};
+
 template <class C, int NORM>
 struct SparseCfg {
-  static constexpr bool KEYS = NORM == ATTN_SPARSEMAX;
+  static constexpr bool KEYS = NORM == ATTN_SPARSEMAX || C::D >= 128;
   static constexpr int LDS_BYTES = C::D == 256 ? 160 * 1024 : 80 * 1024;
   static constexpr int NA = KEYS ? 2 : 3;          // K tiles in flight, threshold passes
+  static constexpr int NX = 3;                     // K tiles in flight, extra passes
   static constexpr int NB = 3;                     // K/V tiles in flight, output pass
   static constexpr int KTILE = C::BN * C::D * 2;   // bytes of one K (or V) tile
   static constexpr int WREG = (LDS_BYTES - NA * KTILE) / C::NW / 256 * 256;  // bytes per wave
   static constexpr int SCAP_F = WREG / 256 / 8 * 8;        // values per lane, no keys
   static constexpr int SCAP_K = WREG / 384 / 8 * 8;        // values per lane with keys
   static constexpr int KEYS_OFF = SCAP_K * 256;            // key indices, from the region start
+  static constexpr int WREG_X = (LDS_BYTES - NX * KTILE) / C::NW / 256 * 256;
+  static constexpr int SCAP_X = WREG_X / 256 / 8 * 8;      // values per lane, extra passes
   static_assert(NB * 2 * KTILE <= LDS_BYTES, "output pass stages must fit");
-  static_assert(SCAP_K >= 32 && KEYS_OFF + SCAP_K * 128 <= WREG && SCAP_F >= 32, "candidate buffer too small");
+  static_assert(SCAP_K >= 32 && KEYS_OFF + SCAP_K * 128 <= WREG && SCAP_X >= 32 && SCAP_X <= SCAP_F,
+                "candidate buffer too small");
+  static_assert(NA <= NX, "extra passes take at least the stages of pass A");
 };
 
 typedef unsigned short u16;
@@ -1067,7 +1079,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
 
   // ---- pass A: row max, floor and candidates --------------------------------
   char* const region = (char*)(lds + SC::NA * KT) + wave * SC::WREG;
-  float* const buf = (float*)region + lane;
+  float* buf = (float*)region + lane;  // moves for the extra passes
   u16* const kbuf = (u16*)(region + SC::KEYS_OFF) + lane;
   float mrun = -INFINITY;     // running max of z over the row (both lanes)
   double floor_ = -INFINITY;  // lower bound on tau (z units)
@@ -1203,32 +1215,38 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     ts.n = t1 - t0;
   }
   auto tile_at = [&](int u) { return u < ts.n ? ts.tile(u) : -1; };
-  auto k_prologue = [&]() __attribute__((always_inline)) {
+  // (the stage count NS comes in as the type of the first argument)
+  auto k_prologue = [&](auto ns) __attribute__((always_inline)) {
+    constexpr int NS = decltype(ns)::value;
 #pragma unroll
-    for (int u = 0; u < NA - 1; ++u) {
+    for (int u = 0; u < NS - 1; ++u) {
       const int tt = tile_at(u);
       dma.issue_k(rk, ka_of(u), tt * C::BN, tt >= 0, pg);
     }
     wait_vmcnt<0>();
     lds_barrier();
   };
-  // start of step u: K of position u + NA - 1 into the stage position u - 1 left
-  auto k_next = [&](int u, int cur) __attribute__((always_inline)) {
-    const int nxt = cur == 0 ? NA - 1 : cur - 1;
-    const int tn = tile_at(u + NA - 1);
+  // start of step u: K of position u + NS - 1 into the stage position u - 1 left
+  auto k_next = [&](auto ns, int u, int cur) __attribute__((always_inline)) {
+    constexpr int NS = decltype(ns)::value;
+    const int nxt = cur == 0 ? NS - 1 : cur - 1;
+    const int tn = tile_at(u + NS - 1);
     dma.issue_k(rk, ka_of(nxt), tn * C::BN, tn >= 0, pg);
   };
   // end of step t: this wave's part of tile t + 1 has landed, then the barrier
-  auto k_done = [&](int& cur) __attribute__((always_inline)) {
-    wait_vmcnt<(NA - 2) * DmaTiles<C>::NI>();
+  auto k_done = [&](auto ns, int& cur) __attribute__((always_inline)) {
+    constexpr int NS = decltype(ns)::value;
+    wait_vmcnt<(NS - 2) * DmaTiles<C>::NI>();
     lds_barrier();
-    cur = cur == NA - 1 ? 0 : cur + 1;
+    cur = cur == NS - 1 ? 0 : cur + 1;
   };
-  k_prologue();
+  constexpr Stages<NA> sa{};
+  constexpr Stages<SC::NX> sx{};
+  k_prologue(sa);
   int cur = 0;
   for (int u = 0; u < ts.n; ++u) {
     const bf16_t* kl = ka_of(cur);
-    k_next(u, cur);
+    k_next(sa, u, cur);
     const int t = ts.tile(u);
     const int k0 = t * C::BN;
     const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
@@ -1302,39 +1320,23 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             if (__any(full)) ovf = ovf || (full | partner_i(full)) != 0;
           }
           if (!ovf) {
+            // only the accepting lanes write: a 16-key block rarely holds
+            // more than one or two candidates of a row, and the writes of a
+            // value no lane accepts are skipped altogether
             const int kk = s_key(k0, kb, 0, g);  // key of value 0; value r adds s_key(0, 0, r, 0)
-            if (cnt + 16 <= cap) {
-              // branch-free: every value is written at the append position,
-              // which only advances for the accepted ones
-              if (SC::KEYS && keyed) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  buf[cnt * 64] = v[r];
-                  kbuf[cnt * 64] = (u16)(kk + s_key(0, 0, r, 0));
-                  cnt += v[r] > floor_v ? 1 : 0;
-                }
-              } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  buf[cnt * 64] = v[r];
-                  cnt += v[r] > floor_v ? 1 : 0;
-                }
-              }
-            } else {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                if (v[r] > floor_v) {
-                  buf[cnt * 64] = v[r];
-                  if (SC::KEYS && keyed) kbuf[cnt * 64] = (u16)(kk + s_key(0, 0, r, 0));
-                  ++cnt;
-                }
+            for (int r = 0; r < 16; ++r) {
+              if (v[r] > floor_v) {
+                buf[cnt * 64] = v[r];
+                if (SC::KEYS && keyed) kbuf[cnt * 64] = (u16)(kk + s_key(0, 0, r, 0));
+                ++cnt;
               }
             }
           }
         }
       }
     }
-    k_done(cur);
+    k_done(sa, cur);
   }
   wait_vmcnt<0>();
 
@@ -1384,29 +1386,43 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // values above it into the lane buffers.  When both halves fit, the row is
   // solved exactly from the buffers as above; otherwise the totals give one
   // threshold step and the next pass starts from the raised floor.
-  // workgroup OR through one word of the last K stage (idle here: every
-  // transfer has landed); the runtime's __syncthreads_or would take static LDS
-  // on top of the dynamic allocation and cost the second workgroup per CU
-  int* const any_word = (int*)ka_of(NA - 1);
+  // workgroup OR through one word of K stage 0 (idle here: every transfer has
+  // landed, and the closing barrier keeps the next transfers from landing
+  // before every wave has read it); the runtime's __syncthreads_or would
+  // take static LDS on top of the dynamic allocation and cost the second
+  // workgroup per CU
+  int* const any_word = (int*)ka_of(0);
   auto block_any = [&](bool v) __attribute__((always_inline)) {
     __syncthreads();
     if (tid == 0) *(volatile int*)any_word = 0;
     __syncthreads();
     if (v) *(volatile int*)any_word = 1;
     __syncthreads();
-    return *(volatile int*)any_word != 0;
+    const bool r = *(volatile int*)any_word != 0;
+    __syncthreads();
+    return r;
   };
+  bool first_x = true;
   while (block_any(pending)) {
+    if (SC::NX != NA && first_x) {
+      // pass A's buffers are dead: a wave with a pending row has dropped its
+      // keys, so the output runs on the matrix cores
+      first_x = false;
+      buf = (float*)((char*)(lds + SC::NX * KT) + wave * SC::WREG_X) + lane;
+      keyed = false;
+      cap = SC::SCAP_X;
+      cnt = 0;
+    }
     double c = 0.0, s1 = 0.0, s2 = 0.0;
     float mn = INFINITY;
     const double mref = (double)mrun;
     if (pending) cnt = 0;  // solved rows keep their support
     int fits = pending ? 1 : 0;
-    k_prologue();
+    k_prologue(sx);
     cur = 0;
     for (int u = 0; u < ts.n; ++u) {
       const bf16_t* kl = ka_of(cur);
-      k_next(u, cur);
+      k_next(sx, u, cur);
       const int t = ts.tile(u);
       const int k0 = t * C::BN;
       const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(pending);
@@ -1457,7 +1473,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           }
         }
       }
-      k_done(cur);
+      k_done(sx, cur);
     }
     wait_vmcnt<0>();
     c += partner_d(c);
