@@ -22,27 +22,14 @@
 
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace attn {
 namespace {
 
 constexpr int kMaxD = 256;
-
-struct BwdArgs {
-  FwdArgs f;
-  const void* dout;
-  void* dq;
-  void* dk;
-  void* dv;
-  int64_t do_sb, do_sh, do_sl;
-  int64_t dq_sb, dq_sh, dq_sl;
-  int64_t dk_sb, dk_sh, dk_sl;
-  int64_t dv_sb, dv_sh, dv_sl;
-  float* dsinks;
-  float* crow;   // workspace: c_i per query row
-  float* srow;   // workspace: -p_sink,i c_i per query row (softmax1 with sinks)
-};
 
 // Weight of one score from the row statistics, and u = sqrt(p) for entmax.
 template <int NORM>
@@ -270,6 +257,11 @@ __global__ __launch_bounds__(64) void bwd_sink_kernel(BwdArgs w) {
   if (lane == 0) w.dsinks[h] = s;
 }
 
+hipError_t launch_bwd_sinks(const BwdArgs& w, hipStream_t stream) {
+  bwd_sink_kernel<<<dim3((unsigned)w.f.Hq), dim3(64), 0, stream>>>(w);
+  return hipGetLastError();
+}
+
 template <typename T, int NORM>
 hipError_t launch_norm(const BwdArgs& w, hipStream_t stream) {
   const FwdArgs& a = w.f;
@@ -343,8 +335,11 @@ static int bwd_prepare(const attn_tensor* q, const attn_tensor* k, const attn_te
   return ATTN_OK;
 }
 
-static size_t bwd_workspace(const BwdArgs& w) {
-  return (size_t)w.f.B * w.f.Hq * w.f.Lq * 2 * sizeof(float);
+// Per-row path: c_i and the sink term per query row.  Matrix-core path: the
+// record blocks, then the sink term per query row.
+static size_t bwd_workspace(const FwdArgs& a) {
+  const size_t rows = (size_t)a.B * a.Hq * a.Lq;
+  return std::max(rows * 2 * sizeof(float), bwd_mfma_rec_bytes(a) + rows * sizeof(float));
 }
 
 extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -356,15 +351,25 @@ extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_t
   if (st) return st;
   if (dsinks && w.f.norm != ATTN_SOFTMAX1)
     return bwd_fail(ATTN_E_INVALID, "sink gradients apply to softmax1 only");
-  const size_t need = bwd_workspace(w);
+  const size_t need = bwd_workspace(w.f);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return bwd_fail(ATTN_E_WORKSPACE, "workspace smaller than attn_bwd_workspace_bytes()");
-  w.crow = (float*)workspace;
-  w.srow = w.crow + (size_t)w.f.B * w.f.Hq * w.f.Lq;
   w.dsinks = dsinks;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const hipError_t e = w.f.dtype == ATTN_BF16 ? launch_t<bf16_t>(w, s) : launch_t<float>(w, s);
+  hipError_t e;
+  if (bwd_mfma_supported(w)) {
+    w.rec = (float*)workspace;
+    w.rec_bytes = bwd_mfma_rec_bytes(w.f);
+    w.srow = (float*)((char*)workspace + w.rec_bytes);
+    e = launch_bwd_mfma(w, s);
+    if (e == hipSuccess && w.dsinks && w.f.Hq)
+      e = launch_bwd_sinks(w, s);
+  } else {
+    w.crow = (float*)workspace;
+    w.srow = w.crow + (size_t)w.f.B * w.f.Hq * w.f.Lq;
+    e = w.f.dtype == ATTN_BF16 ? launch_t<bf16_t>(w, s) : launch_t<float>(w, s);
+  }
   if (e != hipSuccess) return bwd_fail(ATTN_E_LAUNCH, "HIP launch failed");
   return ATTN_OK;
 }
@@ -375,6 +380,6 @@ extern "C" int attn_bwd_workspace_bytes(const attn_tensor* q, const attn_tensor*
   FwdArgs a;
   int st = validate_fwd_args(q, k, v, p, &a, false);
   if (st) return st;
-  *bytes = (size_t)a.B * a.Hq * a.Lq * 2 * sizeof(float);
+  *bytes = bwd_workspace(a);
   return ATTN_OK;
 }

@@ -130,9 +130,34 @@ __device__ __forceinline__ void key_range(int i, int lq, int live, int causal, i
   hi = h;
 }
 
+// Arguments of the backward: the forward's (with row_stats in f.stats), the
+// upstream gradient, the three gradients (strides in elements) and the
+// workspace rows.
+struct BwdArgs {
+  FwdArgs f;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t do_sb, do_sh, do_sl;
+  int64_t dq_sb, dq_sh, dq_sl;
+  int64_t dk_sb, dk_sh, dk_sl;
+  int64_t dv_sb, dv_sh, dv_sl;
+  float* dsinks;
+  float* crow;   // workspace: c_i per query row (per-row kernels)
+  float* srow;   // workspace: -p_sink,i c_i per query row (softmax1 with sinks)
+  float* rec;    // workspace: per-row records of the matrix-core kernels
+  size_t rec_bytes;
+};
+
 // Launchers, one per kernel family (defined in their own translation units).
 hipError_t launch_generic(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const FwdArgs& a, hipStream_t stream);
+// Matrix-core backward (bf16, D = 64 or 128, contiguous K/V): query kernel
+// (row constants, records, dQ) then key kernel (dK, dV).
+bool bwd_mfma_supported(const BwdArgs& w);
+size_t bwd_mfma_rec_bytes(const FwdArgs& a);
+hipError_t launch_bwd_mfma(const BwdArgs& w, hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, void* workspace, hipStream_t stream);
 size_t decode_workspace_bytes(const FwdArgs& a);
 bool prefill_mfma_supported(const FwdArgs& a);

@@ -27,71 +27,10 @@
 // and value 0, i.e. the running max starts at 0 and the running sum at 1
 // ("HF Attention Normalizers", "Important Limitations").
 
-#include "common.h"
+#include "tiles.h"
 
 namespace attn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <int D_, int BN_, int NW_>
-struct Cfg {
-  static constexpr int D = D_, BN = BN_, NW = NW_;
-  static constexpr int NT = NW * 64;          // threads per workgroup
-  static constexpr int BM = NW * 32;          // query rows per workgroup
-  static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-  static constexpr int KCH = BN * CPR;        // chunks per K tile
-  static constexpr int NKB = BN / 32;         // 32-key blocks per tile
-  static constexpr int NDB = D / 32;          // 32-dim blocks of the output
-  static constexpr int NQC = D / 16;          // 16-dim steps of QK^T
-  static_assert(CPR >= 8, "head dim must be >= 64");
-  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
-};
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Value held by the partner lane (l ^ 32), through v_permlane32_swap (no LDS
-// round trip).  The swap returns this lane's value and the partner's in its
-// two result slots; the slot that differs from the own value is the
-// partner's (if the two are equal the choice does not matter).
-__device__ __forceinline__ unsigned partner_u(unsigned x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return r[0] == x ? r[1] : r[0];
-}
-__device__ __forceinline__ float partner(float x) { return __uint_as_float(partner_u(__float_as_uint(x))); }
-
-// XOR swizzle of 16-byte chunks inside an LDS row of K.  The 64 LDS banks
-// (256 bytes) serve 16 lanes of a 16-byte read per cycle, and those lanes
-// read 16 consecutive rows at one logical chunk: with 128-byte rows (D = 64)
-// rows of equal parity share a bank window, so the chunk is XORed with
-// (row / 2) mod 8; with rows of 256 bytes or more, with row mod 16.
-template <int D>
-__device__ __forceinline__ int k_chunk(int row, int ch) {
-  return ch ^ (D == 64 ? (row >> 1) & 7 : row & 15);
-}
-
-struct RowBounds {
-  int lo, hi;  // visible keys [lo, hi) of one query row
-};
-
-__device__ __forceinline__ RowBounds row_bounds(int q, int Lq, int Lk, int causal, int window) {
-  RowBounds r;
-  const int qp = q + Lk - Lq;
-  int hi = causal ? min(Lk, qp + 1) : Lk;
-  hi = max(hi, 0);
-  int lo = window ? max(0, qp - window + 1) : 0;
-  r.lo = min(lo, hi);
-  r.hi = hi;
-  return r;
-}
 
 // Maps the hardware workgroup id to (batch*head, q-block).  Workgroups are
 // dealt round-robin to the 8 XCDs; renumbering gives every XCD a contiguous
@@ -146,147 +85,11 @@ __device__ __forceinline__ SeqSpan seq_span(const FwdArgs& a, int b, int h) {
   return s;
 }
 
-template <class C>
-__device__ __forceinline__ void qk_tile(const bf16_t* kl, const bf16x8* qreg, int l32, int g,
-                                        f32x16* s) {
-  // operand reads are issued in groups of QG ahead of the MFMAs that use them
-  constexpr int NOP = C::NQC * C::NKB;
-  constexpr int QG = NOP < 8 ? NOP : 8;
-#pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-  for (int g0 = 0; g0 < NOP; g0 += QG) {
-    bf16x8 kv[QG];
-#pragma unroll
-    for (int j = 0; j < QG; ++j) {
-      const int c = (g0 + j) / C::NKB, kb = (g0 + j) % C::NKB;
-      const int row = kb * 32 + l32;
-      kv[j] = *(const bf16x8*)(kl + row * C::D + k_chunk<C::D>(row, 2 * c + g) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < QG; ++j) {
-      const int c = (g0 + j) / C::NKB, kb = (g0 + j) % C::NKB;
-      s[kb] = mfma(kv[j], qreg[c], s[kb]);
-    }
-  }
-}
-
-__device__ __forceinline__ int s_key(int k0, int kb, int r, int g) {
-  return k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Max / sum over the two lanes that share a query row (lanes l and l ^ 32):
-// v_permlane32_swap hands each half the other half's value.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Two floats to a packed pair of bf16 (round to nearest even).
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-// P operand of PV step t = 2 kb + h from the 16 S^T values of block kb.
-__device__ __forceinline__ bf16x8 p_operand(const float* p8) {
-  const u32x4 w = {pack_bf16(p8[0], p8[1]), pack_bf16(p8[2], p8[3]), pack_bf16(p8[4], p8[5]),
-                   pack_bf16(p8[6], p8[7])};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-// logit softcap in the log2 domain: log2(e) * cap * tanh(raw * scaling / cap)
-__device__ __forceinline__ float capped_log2(float raw, float sc_over_cap, float cap_log2e) {
-  const float y = raw * sc_over_cap;
-  const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);  // exp(2y)
-  const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);  // tanh(y)
-  return cap_log2e * t;
-}
-
-// z of one raw score q.k (the value the threshold acts on).
-// Monotone in raw (cz, capz > 0); a masked score (-inf) stays -inf.
-template <bool CAP>
-__device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, float capz) {
-#pragma clang fp contract(off)
-  if (CAP) {
-    const float y = raw * sc_over_cap;
-    const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
-    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
-    return raw == -INFINITY ? -INFINITY : capz * t;
-  }
-  return raw * cz;
-}
-
 // Lazy rescaling: the accumulators O and l are kept relative to a reference
 // max m_use that only moves when the running max exceeds it by more than
 // kRescale (log2 units), so most tiles skip the O *= alpha pass; weights
 // stay <= 2^kRescale.  The true running max is tracked for row_stats.
 constexpr float kRescale = 8.f;
-
-// Direct global -> LDS staging for the softmax family (buffer_load ... lds):
-// no staging registers and no vector-ALU work, so NBUF tiles can be in flight.
-// One transfer moves 1 KB per wave; lane l's 16 bytes land at byte 16 l of
-// the destination, and the lane's source chunk is chosen so that the LDS
-// image of a tile is row-major with an XOR chunk swizzle:
-//   K: chunk c of key r at position k_chunk(r, c)
-//   V: chunk c of key r at position c ^ v_swz(r)
-// Keys past the end of the sequence read as zeros (buffer range check, which
-// covers the scalar offset too); a transfer that is not needed is sent wholly
-// out of range, so every wave issues the same number per tile.
-//
-// The transfer is issued from inline assembly, so the compiler neither sees
-// it as an LDS write nor counts it: every wait for it is explicit (wait_vmcnt
-// before the barrier that publishes a tile).  Left to the compiler, a
-// transposing LDS read would wait for all transfers in flight, the prefetch
-// included.  Compiler-counted waits stay correct, since vector-memory loads
-// complete in issue order and extra loads only make a vmcnt wait stricter.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor (stride 0, num_records = bytes) in scalar registers.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)base;
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
-               __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu)),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-
-// 16 bytes per lane from buffer offset voff + soff to LDS byte lds_addr + 16 l.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-template <class C>
-__device__ __forceinline__ int v_swz(int r) { return C::D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
-
-// s_waitcnt for "at most N vector-memory operations of this wave in flight"
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier without the release/acquire fences of __syncthreads()
-// (which would wait for every transfer in flight); LDS hazards are covered by
-// explicit vmcnt waits and by each wave consuming its LDS reads before it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Paged K/V (chunked prefill through the block table).  One transfer covers
 // 64 / CPR consecutive keys, which lie in one page when the block size is a
@@ -831,6 +634,14 @@ __device__ __forceinline__ double thr_step(double c, double s1, double s2, float
   }
   exact = false;
   return mref + fmax(step, mny);
+}
+
+// f(t) = sum over {z > t} of g(z - t) - 1 from the totals of that set about
+// mref (count c, sums s1, s2 of z - mref), ty = t - mref.  f is convex and
+// decreasing in t, positive below tau and not positive from tau on.
+template <int NORM>
+__device__ __forceinline__ double thr_f(double c, double s1, double s2, double ty) {
+  return NORM == ATTN_SPARSEMAX ? s1 - c * ty - 1.0 : s2 - 2.0 * ty * s1 + c * ty * ty - 1.0;
 }
 
 // Largest float not above x.
@@ -1402,6 +1213,23 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     __syncthreads();
     return r;
   };
+  // Bracket of a pending row: floor_ <= tau <= ub.  Each pass also takes the
+  // totals above hi (floor_ < hi <= ub, +inf at first) and collects only the
+  // values in the window (floor_, hi].  When f(hi) <= 0 and the window fits,
+  // the row is solved exactly from the window plus the totals above hi.
+  // Otherwise the floor takes a left-Newton step (from hi as well when
+  // f(hi) > 0), the secant through the best known points on both sides
+  // bounds tau from above (f is convex), and the next window is the whole
+  // bracket when a linear count model says it fits, else its lower part.
+  double hi_ = INFINITY;     // window top (z units)
+  float hi_v = INFINITY;     // the same test in the stored domain
+  double ub = (double)mrun;  // point with f(ub) = fub <= 0 known
+  double fub = -1.0;         // (no key lies above the row max)
+  auto set_hi = [&](double x) __attribute__((always_inline)) {
+    hi_ = x;
+    const float xf = float_floor(x);
+    hi_v = CAP ? xf : raw_floor(xf, cz);
+  };
   bool first_x = true;
   while (block_any(pending)) {
     if (SC::NX != NA && first_x) {
@@ -1413,8 +1241,9 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       cap = SC::SCAP_X;
       cnt = 0;
     }
-    double c = 0.0, s1 = 0.0, s2 = 0.0;
-    float mn = INFINITY;
+    double c = 0.0, s1 = 0.0, s2 = 0.0;      // above the floor
+    double ch = 0.0, s1h = 0.0, s2h = 0.0;   // above hi
+    float mn = INFINITY, mnh = INFINITY;
     const double mref = (double)mrun;
     if (pending) cnt = 0;  // solved rows keep their support
     int fits = pending ? 1 : 0;
@@ -1449,6 +1278,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
                 s1 += y;
                 s2 += y * y;
                 mn = fminf(mn, z);
+                if (v > hi_v) {
+                  ch += 1.0;
+                  s1h += y;
+                  s2h += y * y;
+                  mnh = fminf(mnh, z);
+                }
               }
             }
           }
@@ -1459,7 +1294,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
             for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                if (vv[kb][r] > floor_v) {
+                if (vv[kb][r] > floor_v && !(vv[kb][r] > hi_v)) {
                   if (cnt < cap) {
                     buf[cnt * 64] = vv[kb][r];
                     if (SC::KEYS && keyed) kbuf[cnt * 64] = (u16)s_key(k0, kb, r, g);
@@ -1480,8 +1315,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     s1 += partner_d(s1);
     s2 += partner_d(s2);
     mn = fminf(mn, partner(mn));
+    ch += partner_d(ch);
+    s1h += partner_d(s1h);
+    s2h += partner_d(s2h);
+    mnh = fminf(mnh, partner(mnh));
     fits = fits & partner_i(fits);
-    if (pending && !fits) {
+    const double fh = hi_ < INFINITY ? thr_f<NORM>(ch, s1h, s2h, hi_ - mref) : -1.0;
+    bool solving = pending && fits && fh <= 0.0;
+    if (pending && !solving) {
       bool ex;
       const double tn = thr_step<NORM>(c, s1, s2, mn, mref, floor_, ex);
       if (ex) {
@@ -1490,10 +1331,43 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         pending = false;
         cnt = 0;
       } else {
-        if (tn > floor_) set_floor(tn);
+        double lo = fmax(tn, floor_);
+        double tl = floor_, fl = thr_f<NORM>(c, s1, s2, floor_ - mref);  // best point below tau
+        bool ex2 = false;
+        if (fh > 0.0) {  // hi lies below tau
+          const double tn2 = thr_step<NORM>(ch, s1h, s2h, mnh, mref, hi_, ex2);
+          if (ex2) {
+            tau = tn2;
+            ksup = (int)ch;
+            pending = false;
+            cnt = 0;
+          } else {
+            lo = fmax(lo, fmax(tn2, hi_));
+            tl = hi_;
+            fl = fh;
+          }
+        } else if (hi_ < ub) {
+          ub = hi_;
+          fub = fh;
+        }
+        if (!ex2) {
+          // secant through (tl, fl > 0) and (ub, fub <= 0): an upper bound on tau
+          double top = ub;
+          if (fl > fub) {
+            const double sec = tl + fl * (ub - tl) / (fl - fub);
+            if (sec >= lo && sec < top) top = sec;
+          }
+          // row counts above the floor and above hi (or none above the max),
+          // linear in between: the estimated count of (lo, top]
+          const double ta = floor_, tb = hi_ < INFINITY ? hi_ : mref;
+          const double cb = hi_ < INFINITY ? ch : 0.0;
+          const double est = tb > ta ? (c - cb) * (top - lo) / (tb - ta) : c;
+          const double budget = 1.5 * cap;  // two lanes' buffers, with a margin for imbalance
+          set_floor(lo);
+          set_hi(est <= budget ? top : lo + (top - lo) * (budget / est));
+        }
       }
     }
-    bool solving = pending && fits;
     for (int it = 0; it < 2 * SC::SCAP_F + 4; ++it) {
       if (!__any(solving)) break;
       double cc, a1, a2;
@@ -1504,6 +1378,11 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       a2 += partner_d(a2);
       m1 = fminf(m1, partner(m1));
       if (solving) {
+        // the window's values above the floor plus everything above hi
+        cc += ch;
+        a1 += s1h;
+        a2 += s2h;
+        m1 = fminf(m1, mnh);
         bool ex;
         const double tn = thr_step<NORM>(cc, a1, a2, m1, mref, floor_, ex);
         if (ex) {
@@ -1512,6 +1391,15 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           solving = false;
           pending = false;
           inbuf = true;
+        } else if (tn > hi_) {
+          // a step never passes tau, so hi lay below it after all (f(hi)
+          // within rounding of 0): hi is a floor; the passes go on
+          set_floor(hi_);
+          set_hi(INFINITY);
+          ub = mref;
+          fub = -1.0;
+          solving = false;
+          cnt = 0;
         } else {
           if (tn > floor_) set_floor(tn);
         }

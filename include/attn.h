@@ -238,9 +238,12 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  * contiguous.  The sparse normalizers' gradients are the usual ones of the
  * piecewise-smooth maps (sparsemax: dP minus its mean over the support, on
  * the support; 1.5-entmax: sqrt(p) (dP - sum sqrt(p) dP / sum sqrt(p))).
- * Contiguous K/V, no block mask.  fp32 arithmetic on the per-row kernels;
- * every output is written in full.  workspace: attn_bwd_workspace_bytes
- * (8 bytes per query row).  Errors as attn_fwd.                           */
+ * Contiguous K/V, no block mask.  bf16 inputs with D = 64 or 128 (16-byte
+ * aligned, strides multiples of 8 elements) run on the matrix cores (bf16
+ * operands, fp32 accumulation); everything else on per-row fp32 kernels.
+ * Every output is written in full.  workspace: attn_bwd_workspace_bytes
+ * (the larger of 8 bytes per query row, and 768 bytes per 64 query rows of
+ * each (batch, head) plus 4 bytes per query row).  Errors as attn_fwd.    */
 int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
              const attn_tensor* dout, const float* row_stats, const attn_params* p,
              const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,

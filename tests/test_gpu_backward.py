@@ -1,7 +1,9 @@
 """GPU parity of the backward (attn_bwd): dq, dk, dv (and softmax1 sink
 gradients) against the float64 backward oracle, from the row statistics the
 GPU forward saved.  f32 and bf16 inputs, GQA, Lq != Lk, causal / window /
-softcap.  Sparsemax rows are drawn so that no score lies within 1e-4 of the
+softcap.  bf16 at head dim 64 and 128 runs the matrix-core kernels (several
+key and query tiles, ragged ends, rows without keys); other cases the
+per-row kernels.  Sparsemax rows are drawn so that no score lies within 1e-4 of the
 row's threshold (its Jacobian jumps when a key crosses the support edge, so
 a rounding-level difference there is not a parity error)."""
 
@@ -36,8 +38,8 @@ def _clear_of_edges(q, k, v, norm, causal, window, cap, scaling):
                for r, (idx, p, z) in enumerate(det))
 
 
-def _check(norm, dtype, D, causal, window, cap, seed, sinks=None):
-    B, Hq, Hkv, Lq, Lk = 2, 4, 2, 70, 90
+def _check(norm, dtype, D, causal, window, cap, seed, sinks=None, shape=(2, 4, 2, 70, 90)):
+    B, Hq, Hkv, Lq, Lk = shape
     scaling = 1.0 / math.sqrt(D)
     for s in range(seed, seed + 20):
         q, k, v, do = _inputs(s, B, Hq, Hkv, Lq, Lk, D, dtype)
@@ -81,3 +83,23 @@ def test_masks_and_softcap(norm, causal, window, cap):
 def test_softmax1_sink_gradients():
     _check("softmax1", torch.float32, 64, True, 0, 0.0, 300, sinks=[0.5, -1.0, 2.0, 0.0])
     _check("softmax1", torch.bfloat16, 64, True, 0, 0.0, 301, sinks=[1.5, 0.0, -0.5, 3.0])
+
+
+@pytest.mark.parametrize("norm", NORMS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal,window,cap", [(False, 0, 0.0), (True, 20, 0.0), (True, 0, 5.0),
+                                               (True, 150, 30.0)])
+def test_mfma_masks_and_softcap(norm, D, causal, window, cap):
+    _check(norm, torch.bfloat16, D, causal, window, cap, 400 + D)
+
+
+@pytest.mark.parametrize("norm", NORMS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("shape", [(1, 4, 1, 200, 333), (1, 2, 2, 300, 300), (2, 2, 1, 150, 100)],
+                         ids=["gqa4_lq200_lk333", "mha_300", "lq150_lk100_empty_rows"])
+def test_mfma_multi_tile(norm, D, shape):
+    _check(norm, torch.bfloat16, D, True, 0, 0.0, 500 + D, shape=shape)
+
+
+def test_mfma_sink_gradients():
+    _check("softmax1", torch.bfloat16, 128, True, 0, 0.0, 302, sinks=[0.5, -1.0, 2.0, 0.0])
