@@ -334,7 +334,9 @@ struct KeyLds {
 };
 
 template <class C, int NORM, bool CAP>
-__global__ __launch_bounds__(C::NT, 2) void bwd_key_mfma(BwdArgs w) {
+// D = 128: K, V and the dK, dV accumulators need more than the 256 registers
+// of two waves per SIMD, so one wave per SIMD (no spills)
+__global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdArgs w) {
   static_assert(C::BN == kRecRows, "a query tile is one record block");
   const FwdArgs& a = w.f;
   constexpr int QT = C::BN * C::D;            // elements of one Q (or dO) tile
