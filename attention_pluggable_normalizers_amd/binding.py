@@ -83,9 +83,9 @@ def load_library(path=None):
     lib.attn_fwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged),
                                              P(_Params), P(ctypes.c_size_t)]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_int
-    lib.attn_bwd.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_void_p,
-                             P(_Params), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_void_p,
-                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_bwd.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor),
+                             ctypes.c_void_p, P(_Params), P(_Tensor), P(_Tensor), P(_Tensor),
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Params),
                                              P(ctypes.c_size_t)]
@@ -282,11 +282,14 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
 
 
 def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, softcap=0.0,
-             scaling=None, sinks=None, dq=None, dk=None, dv=None, sink_grad=False, stream=None):
+             scaling=None, sinks=None, dq=None, dk=None, dv=None, sink_grad=False, out=None,
+             stream=None):
     """Gradients of ``attn_fwd`` for the same q, k, v and parameters, given the
     forward's ``row_stats`` and the upstream gradient ``dout``: returns
     ``(dq, dk, dv, dsinks)`` (``dsinks`` float32 [Hq] when ``sink_grad``,
-    softmax1 only, else None)."""
+    softmax1 only, else None).  ``out`` (optional): the forward's output; the
+    softmax family then takes its row constant from dout . out (one pass
+    fewer)."""
     lib = load_library()
     if (row_stats is None or row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
             or tuple(row_stats.shape) != (*q.shape[:3], 2)):
@@ -303,7 +306,8 @@ def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, so
     ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib.attn_bwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+    od = ctypes.byref(_desc(out)) if out is not None else None
+    _check(lib.attn_bwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), od,
                         ctypes.byref(_desc(dout)), row_stats.data_ptr(), ctypes.byref(p),
                         ctypes.byref(_desc(dq)), ctypes.byref(_desc(dk)), ctypes.byref(_desc(dv)),
                         ds.data_ptr() if ds is not None else None, ws.data_ptr(), n.value,

@@ -302,7 +302,8 @@ static int same_shape(const attn_tensor* a, const attn_tensor* b) {
 }
 
 static int bwd_prepare(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
-                       const attn_tensor* dout, const float* row_stats, const attn_params* p,
+                       const attn_tensor* out, const attn_tensor* dout, const float* row_stats,
+                       const attn_params* p,
                        const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
                        BwdArgs* w, bool need_data) {
   memset(w, 0, sizeof(*w));
@@ -312,6 +313,14 @@ static int bwd_prepare(const attn_tensor* q, const attn_tensor* k, const attn_te
   if (!dout || !dq || !dk || !dv) return bwd_fail(ATTN_E_INVALID, "dout, dq, dk or dv descriptor is NULL");
   if (!same_shape(dout, q) || !same_shape(dq, q))
     return bwd_fail(ATTN_E_INVALID, "dout and dq must match q in shape and dtype");
+  if (out) {
+    if (!same_shape(out, q)) return bwd_fail(ATTN_E_INVALID, "out must match q in shape and dtype");
+    if (out->stride[3] != 1) return bwd_fail(ATTN_E_INVALID, "out needs a contiguous last dimension");
+    for (int d = 0; d < 4; ++d)
+      if (out->stride[d] < 0) return bwd_fail(ATTN_E_INVALID, "out has a negative stride");
+    if (need_data && !out->data && out->shape[0] * out->shape[1] * out->shape[2] * out->shape[3] != 0)
+      return bwd_fail(ATTN_E_INVALID, "out data pointer is NULL");
+  }
   if (!same_shape(dk, k) || !same_shape(dv, v))
     return bwd_fail(ATTN_E_INVALID, "dk and dv must match k and v in shape and dtype");
   const attn_tensor* ts[] = {dout, dq, dk, dv};
@@ -332,6 +341,11 @@ static int bwd_prepare(const attn_tensor* q, const attn_tensor* k, const attn_te
   w->dk_sb = dk->stride[0]; w->dk_sh = dk->stride[1]; w->dk_sl = dk->stride[2];
   w->dv_sb = dv->stride[0]; w->dv_sh = dv->stride[1]; w->dv_sl = dv->stride[2];
   w->f.stats = (float*)row_stats;
+  w->have_out = out != nullptr;
+  if (out) {
+    w->f.out = out->data;
+    w->f.o_sb = out->stride[0]; w->f.o_sh = out->stride[1]; w->f.o_sl = out->stride[2];
+  }
   return ATTN_OK;
 }
 
@@ -343,11 +357,12 @@ static size_t bwd_workspace(const FwdArgs& a) {
 }
 
 extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
-                        const attn_tensor* dout, const float* row_stats, const attn_params* p,
-                        const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
-                        float* dsinks, void* workspace, size_t workspace_bytes, void* stream) {
+                        const attn_tensor* out, const attn_tensor* dout, const float* row_stats,
+                        const attn_params* p, const attn_tensor* dq, const attn_tensor* dk,
+                        const attn_tensor* dv, float* dsinks, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   BwdArgs w;
-  int st = bwd_prepare(q, k, v, dout, row_stats, p, dq, dk, dv, &w, true);
+  int st = bwd_prepare(q, k, v, out, dout, row_stats, p, dq, dk, dv, &w, true);
   if (st) return st;
   if (dsinks && w.f.norm != ATTN_SOFTMAX1)
     return bwd_fail(ATTN_E_INVALID, "sink gradients apply to softmax1 only");

@@ -9,7 +9,10 @@
 //              row statistics, and the row constant of the normalizer's
 //              Jacobian (softmax family sum p dP; sparsemax the mean of dP
 //              over the support; 1.5-entmax sum u dP / sum u, u = (z - tau)+),
-//              written with the row's weight parameters to a per-row record
+//              written with the row's weight parameters to a per-row record;
+//              for the softmax family with the forward's output at hand the
+//              constant is dO . O (the weights sum to one and the sink's value
+//              is zero) and the pass is skipped
 //     pass 2   dS^T = w (dP^T - c) through softcap and scaling, and
 //              dQ^T += K^T dS^T (K^T from a transposing LDS read)
 //   key kernel, one workgroup per 128 keys of one (batch, kv head), lane per
@@ -157,8 +160,9 @@ __device__ __forceinline__ void elem(float raw, float r0, float r1, const ElemCo
 
 // ---------------------------------------------------------------------------
 // query kernel
-template <class C, int NORM, bool CAP>
+template <class C, int NORM, bool CAP, bool OUT>
 __global__ __launch_bounds__(C::NT, 2) void bwd_query_mfma(BwdArgs w) {
+  static_assert(!OUT || NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1, "dO . O is the softmax-family constant");
   const FwdArgs& a = w.f;
   constexpr int KT = C::BN * C::D;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * KT];  // 2 stages x (K, V)
@@ -242,6 +246,18 @@ __global__ __launch_bounds__(C::NT, 2) void bwd_query_mfma(BwdArgs w) {
 
   // ---- pass 1: the row constant ---------------------------------------------
   float c1 = 0.f, c2 = 0.f;
+  if (OUT) {
+    // dO . O over this lane's half of the row (the chunks it holds of dO)
+    if (row_ok) {
+      const bf16_t* orow = (const bf16_t*)a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)myq * a.o_sl;
+#pragma unroll
+      for (int c = 0; c < C::NQC; ++c) {
+        const bf16x8 o8 = *(const bf16x8*)(orow + 16 * c + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c1 += (float)o8[e] * (float)doreg[c][e];
+      }
+    }
+  } else
   pass([&](const bf16_t* kl, const bf16_t* vl, int k0) __attribute__((always_inline)) {
     f32x16 s[C::NKB], dp[C::NKB];
     qk_tile<C>(kl, qreg, l32, g, s);
@@ -504,7 +520,13 @@ hipError_t launch_d(const BwdArgs& w, hipStream_t stream) {
   using CK = Cfg<D, 64, 4>;                   // key kernel: query tiles
   const int nqb = (a.Lq + CQ::BM - 1) / CQ::BM;
   const int64_t gq = (int64_t)nqb * a.B * a.Hq;
-  if (gq) bwd_query_mfma<CQ, NORM, CAP><<<dim3((unsigned)gq), dim3(CQ::NT), 0, stream>>>(w);
+  constexpr bool SOFT = NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1;
+  if (gq) {
+    if (SOFT && w.have_out)
+      bwd_query_mfma<CQ, NORM, CAP, SOFT><<<dim3((unsigned)gq), dim3(CQ::NT), 0, stream>>>(w);
+    else
+      bwd_query_mfma<CQ, NORM, CAP, false><<<dim3((unsigned)gq), dim3(CQ::NT), 0, stream>>>(w);
+  }
   const int nkb = (a.Lk + 32 * CK::NW - 1) / (32 * CK::NW);
   const int64_t gk = (int64_t)nkb * a.B * a.Hkv;
   if (gk) {
@@ -537,9 +559,10 @@ bool bwd_mfma_supported(const BwdArgs& w) {
   if (a.dtype != ATTN_BF16 || (a.D != 64 && a.D != 128)) return false;
   if (a.paged || a.cu_q || a.bm_num) return false;
   if (!(a.scaling > 0.f)) return false;
-  const void* ptrs[] = {a.q, a.k, a.v, w.dout, w.dq, w.dk, w.dv};
+  const void* ptrs[] = {a.q, a.k, a.v, w.dout, w.dq, w.dk, w.dv, w.have_out ? a.out : a.q};
   for (const void* p : ptrs)
     if (!aligned16(p)) return false;
+  if (w.have_out && (a.o_sb % 8 || a.o_sh % 8 || a.o_sl % 8)) return false;
   const int64_t s[] = {a.q_sb, a.q_sh, a.q_sl, a.k_sb, a.k_sh, a.k_sl, a.v_sb, a.v_sh, a.v_sl,
                        w.do_sb, w.do_sh, w.do_sl, w.dq_sb, w.dq_sh, w.dq_sl,
                        w.dk_sb, w.dk_sh, w.dk_sl, w.dv_sb, w.dv_sh, w.dv_sl};

@@ -148,6 +148,7 @@ struct BwdArgs {
   float* srow;   // workspace: -p_sink,i c_i per query row (softmax1 with sinks)
   float* rec;    // workspace: per-row records of the matrix-core kernels
   size_t rec_bytes;
+  int have_out;  // f.out / f.o_* hold the forward's output
 };
 
 // Launchers, one per kernel family (defined in their own translation units).

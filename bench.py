@@ -165,8 +165,8 @@ def extra_prefill(apn, W, dev, reps=10):
 
 def backward_bench(apn, cfg, q, k, v, norms, pairs, reps=20):
     """Backward (attn_bwd) of the same workload from the forward's row
-    statistics: median time and TFLOP/s on the conventional 10 * D * pairs
-    (the five products of the backward: scores, dP, dV, dQ, dK)."""
+    statistics and output: median time and TFLOP/s on the conventional
+    10 * D * pairs (the five products of the backward: scores, dP, dV, dQ, dK)."""
     import torch
     g = torch.Generator(device=q.device).manual_seed(cfg.seed + 17)
     do = torch.randn(q.shape, generator=g, device=q.device).to(q.dtype)
@@ -175,9 +175,10 @@ def backward_bench(apn, cfg, q, k, v, norms, pairs, reps=20):
     flops = 10 * cfg.D * pairs
     per = {}
     for n in norms:
-        apn.attn_fwd(q, k, v, None, st, normalizer=n, causal=cfg.causal, scaling=cfg.scaling)
+        out, _ = apn.attn_fwd(q, k, v, None, st, normalizer=n, causal=cfg.causal,
+                              scaling=cfg.scaling)
         f = lambda: apn.attn_bwd(q, k, v, do, st, normalizer=n, causal=cfg.causal,
-                                 scaling=cfg.scaling, dq=dq, dk=dk, dv=dv)
+                                 scaling=cfg.scaling, dq=dq, dk=dk, dv=dv, out=out)
         us = time_launches(f, reps, 3)
         per[n] = {"us": round(us, 1), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 2)}
     return {"workload": cfg.name, "credited_flop_per_launch": flops, "per_normalizer": per}

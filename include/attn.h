@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Status codes. */
 typedef enum attn_status {
@@ -227,8 +227,8 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  * "Important Limitations": the fused backward recomputes the weights from
  * the saved row statistics -- row max and denominator for softmax1, one
  * threshold per row for the sparse normalizers).  For the same q, k, v and
- * parameters as a forward that wrote `row_stats`, and the upstream gradient
- * dout of its output:
+ * parameters as a forward that wrote `row_stats` (and optionally its output
+ * `out`), and the upstream gradient dout of that output:
  *   dq   [B, Hq, Lq, D]  <- dL/dq
  *   dk, dv [B, Hkv, Lk, D] <- dL/dk, dL/dv (summed over each key/value
  *                            head's query heads)
@@ -238,6 +238,10 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  * contiguous.  The sparse normalizers' gradients are the usual ones of the
  * piecewise-smooth maps (sparsemax: dP minus its mean over the support, on
  * the support; 1.5-entmax: sqrt(p) (dP - sum sqrt(p) dP / sum sqrt(p))).
+ * out : NULL, or the forward's output [B, Hq, Lq, D] (dtype of q, last
+ *       dimension contiguous, 16-byte aligned).  softmax / softmax1 then take
+ *       the row constant of the Jacobian, sum_j p dP = dout . out, from it
+ *       and skip one pass over the keys; the sparse normalizers ignore it.
  * Contiguous K/V, no block mask.  bf16 inputs with D = 64 or 128 (16-byte
  * aligned, strides multiples of 8 elements) run on the matrix cores (bf16
  * operands, fp32 accumulation); everything else on per-row fp32 kernels.
@@ -245,7 +249,8 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  * (the larger of 8 bytes per query row, and 768 bytes per 64 query rows of
  * each (batch, head) plus 4 bytes per query row).  Errors as attn_fwd.    */
 int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
-             const attn_tensor* dout, const float* row_stats, const attn_params* p,
+             const attn_tensor* out, const attn_tensor* dout, const float* row_stats,
+             const attn_params* p,
              const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
              float* dsinks, void* workspace, size_t workspace_bytes, void* stream);
 

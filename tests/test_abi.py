@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 4
+    assert apn.attn_abi_version() == 5
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -237,8 +237,9 @@ def test_backward_validation(lib):
     assert n.value == max(2 * 8 * 64 * 8, 2 * 8 * 1 * 768 + 2 * 8 * 64 * 4)
 
     def call(dout=None, dq=None, dk=None, dv=None, stats=0x9000, p=None, dsinks=None, ws=0x9100,
-             wsn=1 << 20):
+             wsn=1 << 20, out=None):
         r = lib.attn_bwd(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv),
+                         ctypes.byref(out) if out is not None else None,
                          ctypes.byref(dout or _t(Q)), stats, ctypes.byref(p or _p()),
                          ctypes.byref(dq or _t(Q)), ctypes.byref(dk or _t(KV)),
                          ctypes.byref(dv or _t(KV)), dsinks, ws, wsn, None)
@@ -253,3 +254,5 @@ def test_backward_validation(lib):
     assert r == 1 and "softmax1" in d
     r, d = call(wsn=8)
     assert r == 3 and "workspace" in d
+    r, d = call(out=_t((2, 8, 64, 32)))
+    assert r == 1 and "out" in d

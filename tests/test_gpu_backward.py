@@ -38,7 +38,8 @@ def _clear_of_edges(q, k, v, norm, causal, window, cap, scaling):
                for r, (idx, p, z) in enumerate(det))
 
 
-def _check(norm, dtype, D, causal, window, cap, seed, sinks=None, shape=(2, 4, 2, 70, 90)):
+def _check(norm, dtype, D, causal, window, cap, seed, sinks=None, shape=(2, 4, 2, 70, 90),
+           use_out=False):
     B, Hq, Hkv, Lq, Lk = shape
     scaling = 1.0 / math.sqrt(D)
     for s in range(seed, seed + 20):
@@ -50,11 +51,11 @@ def _check(norm, dtype, D, causal, window, cap, seed, sinks=None, shape=(2, 4, 2
     qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
     sd = None if sinks is None else torch.tensor(sinks, dtype=torch.float32, device="cuda")
     st = torch.empty(B, Hq, Lq, 2, device="cuda")
-    apn.attn_fwd(qd, kd, vd, None, st, normalizer=norm, causal=causal, window=window,
-                 softcap=cap, scaling=scaling, sinks=sd)
+    out, _ = apn.attn_fwd(qd, kd, vd, None, st, normalizer=norm, causal=causal, window=window,
+                          softcap=cap, scaling=scaling, sinks=sd)
     dq, dk, dv, ds = apn.attn_bwd(qd, kd, vd, dod, st, normalizer=norm, causal=causal,
                                   window=window, softcap=cap, scaling=scaling, sinks=sd,
-                                  sink_grad=sinks is not None)
+                                  sink_grad=sinks is not None, out=out if use_out else None)
     torch.cuda.synchronize()
     ref = attention_backward(q, k, v, do, norm, causal, window, cap, scaling, sinks=sinks)
     for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
@@ -103,3 +104,18 @@ def test_mfma_multi_tile(norm, D, shape):
 
 def test_mfma_sink_gradients():
     _check("softmax1", torch.bfloat16, 128, True, 0, 0.0, 302, sinks=[0.5, -1.0, 2.0, 0.0])
+
+
+@pytest.mark.parametrize("norm", NORMS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal,window,cap", [(True, 0, 0.0), (True, 20, 0.0), (True, 0, 5.0)])
+def test_with_forward_output(norm, D, causal, window, cap):
+    # softmax family: the row constant from dout . out (one pass fewer);
+    # the sparse normalizers ignore out
+    _check(norm, torch.bfloat16, D, causal, window, cap, 600 + D, use_out=True,
+           shape=(1, 4, 2, 150, 200))
+
+
+def test_with_forward_output_sinks():
+    _check("softmax1", torch.bfloat16, 64, True, 0, 0.0, 303, sinks=[0.5, -1.0, 2.0, 0.0],
+           use_out=True)
