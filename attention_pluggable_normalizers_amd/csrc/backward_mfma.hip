@@ -174,8 +174,8 @@ __global__ __launch_bounds__(C::NT, 2) void bwd_query_mfma(BwdArgs w) {
   const int l32 = lane & 31, g = lane >> 5;
   const int Lq = a.Lq, Lk = a.Lk;
   const int nqb = (Lq + C::BM - 1) / C::BM;
-  const int bh = blockIdx.x / nqb;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);  // longest (causal) blocks first
+  int bh, qb;
+  block_coords(nqb, bh, qb);  // per-XCD ranges of heads, longest (causal) blocks first
   const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
   const int q0 = qb * C::BM;
 
@@ -367,7 +367,11 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
   const int Lq = a.Lq, Lk = a.Lk;
   constexpr int BK = 32 * C::NW;  // keys per workgroup
   const int nkb = (Lk + BK - 1) / BK;
-  const int bkv = blockIdx.x / nkb, kblk = (int)(blockIdx.x % nkb);
+  // per-XCD ranges of kv heads (their Q / dO tiles stay in one L2), the
+  // first key blocks -- seen by the most causal queries -- first
+  int bkv, rev;
+  block_coords(nkb, bkv, rev);
+  const int kblk = nkb - 1 - rev;
   const int b = bkv / a.Hkv, kvh = bkv - b * a.Hkv;
   const float* rec_lds = (const float*)(lds + 2 * QT * 2 + wave * 1024);  // + stage offset
 

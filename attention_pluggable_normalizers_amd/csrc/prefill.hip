@@ -32,18 +32,6 @@
 namespace attn {
 namespace {
 
-// Maps the hardware workgroup id to (batch*head, q-block).  Workgroups are
-// dealt round-robin to the 8 XCDs; renumbering gives every XCD a contiguous
-// range of (batch, head) pairs, so the query heads sharing one K/V head stay
-// in one L2, and within a pair the longest (last) q-blocks start first.
-__device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
-  const int nblk = gridDim.x;
-  int id = blockIdx.x;
-  if ((nblk & 7) == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
-  bh = id / nqb;
-  qb = nqb - 1 - (id - bh * nqb);
-}
-
 // Query-row extent of the grid: the longest packed request, or Lq.
 __device__ __host__ __forceinline__ int q_extent(const FwdArgs& a) { return a.cu_q ? a.max_q : a.Lq; }
 

@@ -104,6 +104,18 @@ __device__ __forceinline__ int s_key(int k0, int kb, int r, int g) {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Maps the hardware workgroup id to (batch*head, q-block).  Workgroups are
+// dealt round-robin to the 8 XCDs; renumbering gives every XCD a contiguous
+// range of (batch, head) pairs, so the query heads sharing one K/V head stay
+// in one L2, and within a pair the longest (last) q-blocks start first.
+__device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
+  const int nblk = gridDim.x;
+  int id = blockIdx.x;
+  if ((nblk & 7) == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
+  bh = id / nqb;
+  qb = nqb - 1 - (id - bh * nqb);
+}
+
 // Max / sum over the two lanes that share a query row (lanes l and l ^ 32):
 // v_permlane32_swap hands each half the other half's value.
 __device__ __forceinline__ float pair_max(float x) {
