@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-PREFILL_SRC = os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", "prefill.hip")
+# sources of the prefill kernels (the counter summary is tied to their hash)
+PREFILL_SRCS = [os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", f)
+                for f in ("prefill.hip", "tiles.h", "common.h")]
 
 
 def credited_pairs(cfg):
@@ -97,7 +99,7 @@ def traffic_for(kernel_key):
     the prefill source changed since the counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in PREFILL_SRCS)).hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("prefill_src_sha256") != src or kernel_key not in rec.get("kernels", {}):
