@@ -350,10 +350,17 @@ static int bwd_prepare(const attn_tensor* q, const attn_tensor* k, const attn_te
 }
 
 // Per-row path: c_i and the sink term per query row.  Matrix-core path: the
-// record blocks, then the sink term per query row.
+// record blocks, the sink term per query row, then (G > 1) the fp32 partial
+// dK / dV of every query head.
+// byte offset of the partials: 256-byte aligned (16-byte vector accesses)
+static size_t bwd_part_offset(const FwdArgs& a) {
+  const size_t rows = (size_t)a.B * a.Hq * a.Lq;
+  return (bwd_mfma_rec_bytes(a) + rows * sizeof(float) + 255) / 256 * 256;
+}
+
 static size_t bwd_workspace(const FwdArgs& a) {
   const size_t rows = (size_t)a.B * a.Hq * a.Lq;
-  return std::max(rows * 2 * sizeof(float), bwd_mfma_rec_bytes(a) + rows * sizeof(float));
+  return std::max(rows * 2 * sizeof(float), bwd_part_offset(a) + bwd_mfma_part_bytes(a));
 }
 
 extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -377,6 +384,8 @@ extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_t
     w.rec = (float*)workspace;
     w.rec_bytes = bwd_mfma_rec_bytes(w.f);
     w.srow = (float*)((char*)workspace + w.rec_bytes);
+    w.part = (float*)((char*)workspace + bwd_part_offset(w.f));
+    w.key_split = bwd_key_split(w.f) ? 1 : 0;
     e = launch_bwd_mfma(w, s);
     if (e == hipSuccess && w.dsinks && w.f.Hq)
       e = launch_bwd_sinks(w, s);

@@ -20,6 +20,10 @@
 //   query heads stream through LDS:
 //     S = Q K^T, dP = dO V^T, weights from the records,
 //     dV^T += dO^T P and dK^T += Q^T dS (transposing LDS reads of the tiles).
+//   When that grid is small (under 1024 workgroups, with G > 1) the causal
+//   grid would be too coarse and too unequal to fill the chip: then each
+//   workgroup takes one query head, writes fp32 partial sums, and a small
+//   kernel adds the G partials in head order.
 //
 // w is the Jacobian weight of a score: p for the softmax family, 1 on the
 // support for sparsemax, u for 1.5-entmax; dS = w (dP - c) is the gradient
@@ -367,12 +371,18 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
   const int Lq = a.Lq, Lk = a.Lk;
   constexpr int BK = 32 * C::NW;  // keys per workgroup
   const int nkb = (Lk + BK - 1) / BK;
-  // per-XCD ranges of kv heads (their Q / dO tiles stay in one L2), the
-  // first key blocks -- seen by the most causal queries -- first
-  int bkv, rev;
-  block_coords(nkb, bkv, rev);
+  // per-XCD ranges of heads (the query heads of a kv head are adjacent, so
+  // its K / V rows stay in one L2), the first key blocks -- seen by the most
+  // causal queries -- first
+  int bh, rev;
+  block_coords(nkb, bh, rev);
   const int kblk = nkb - 1 - rev;
-  const int b = bkv / a.Hkv, kvh = bkv - b * a.Hkv;
+  const bool split = w.key_split != 0;  // one query head per workgroup
+  const int nh = split ? a.Hq : a.Hkv;
+  const int b = bh / nh, hx = bh - b * nh;
+  const int kvh = split ? hx / a.G : hx;
+  const int h0 = split ? hx : kvh * a.G;  // first query head of the workgroup
+  const int nheads = split ? 1 : a.G;
   const float* rec_lds = (const float*)(lds + 2 * QT * 2 + wave * 1024);  // + stage offset
 
   // keys of this workgroup, this wave and this lane
@@ -408,11 +418,11 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
   }
   const ElemConst ek = elem_const<NORM, CAP>(a);
 
-  // positions: G query heads x query tiles [qt0, qt1)
+  // positions: nheads query heads x query tiles [qt0, qt1)
   const int qt0 = ilo_g / C::BN;
   const int qt1 = ihi_g > ilo_g ? (ihi_g + C::BN - 1) / C::BN : qt0;
   const int ntq = qt1 - qt0;
-  const int npos = a.G * ntq;
+  const int npos = nheads * ntq;
   RowDma<C> dq_, dd_;
   dq_.init(a.q_sl, wave, lane);
   dd_.init(w.do_sl, wave, lane);
@@ -422,7 +432,7 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
     const bool live = u < npos;
     const int hh = live ? u / ntq : 0;
     const int qt = qt0 + (live ? u - hh * ntq : 0);
-    const int h = kvh * a.G + hh;
+    const int h = h0 + hh;
     const i32x4 rq = rsrc_words((const bf16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh,
                                 (uint32_t)((int64_t)Lq * a.q_sl * 2));
     const i32x4 rd = rsrc_words((const bf16_t*)w.dout + (int64_t)b * w.do_sb + (int64_t)h * w.do_sh,
@@ -498,7 +508,20 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
     lds_barrier();
   }
   wait_vmcnt<0>();
-  if (key_ok) {
+  if (key_ok && split) {
+    // fp32 partials of this query head: [B, Hq, Lk, D] for dK, then for dV
+    const int64_t prow = (((int64_t)b * a.Hq + h0) * Lk + myk) * C::D;
+    const int64_t half = (int64_t)a.B * a.Hq * Lk * C::D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = db * 32 + 8 * rq + 4 * g;
+        *(f32x4*)(w.part + prow + d) = f32x4{dk[db][4 * rq], dk[db][4 * rq + 1], dk[db][4 * rq + 2], dk[db][4 * rq + 3]};
+        *(f32x4*)(w.part + half + prow + d) =
+            f32x4{dv[db][4 * rq], dv[db][4 * rq + 1], dv[db][4 * rq + 2], dv[db][4 * rq + 3]};
+      }
+  } else if (key_ok) {
     bf16_t* dkrow = (bf16_t*)w.dk + (int64_t)b * w.dk_sb + (int64_t)kvh * w.dk_sh + (int64_t)myk * w.dk_sl;
     bf16_t* dvrow = (bf16_t*)w.dv + (int64_t)b * w.dv_sb + (int64_t)kvh * w.dv_sh + (int64_t)myk * w.dv_sl;
 #pragma unroll
@@ -517,6 +540,40 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
   }
 }
 
+// dK, dV of one kv head = the sum of its G query heads' partials, added in
+// head order; one thread per 8 dims of one key row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kv_reduce(BwdArgs w) {
+  const FwdArgs& a = w.f;
+  const int64_t n8 = (int64_t)a.B * a.Hkv * a.Lk * (D / 8);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int d8 = (int)(i % (D / 8));
+  const int64_t row = i / (D / 8);  // (b * Hkv + kvh) * Lk + key
+  const int key = (int)(row % a.Lk);
+  const int64_t bk = row / a.Lk;
+  const int kvh = (int)(bk % a.Hkv), b = (int)(bk / a.Hkv);
+  const int64_t half = (int64_t)a.B * a.Hq * a.Lk * D;
+  f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int64_t src = (((int64_t)b * a.Hq + kvh * a.G + hh) * a.Lk + key) * D + d8 * 8;
+    k0 += *(const f32x4*)(w.part + src);
+    k1 += *(const f32x4*)(w.part + src + 4);
+    v0 += *(const f32x4*)(w.part + half + src);
+    v1 += *(const f32x4*)(w.part + half + src + 4);
+  }
+  bf16x8 ko, vo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ko[e] = (bf16_t)k0[e];
+    ko[e + 4] = (bf16_t)k1[e];
+    vo[e] = (bf16_t)v0[e];
+    vo[e + 4] = (bf16_t)v1[e];
+  }
+  *(bf16x8*)((bf16_t*)w.dk + (int64_t)b * w.dk_sb + (int64_t)kvh * w.dk_sh + (int64_t)key * w.dk_sl + d8 * 8) = ko;
+  *(bf16x8*)((bf16_t*)w.dv + (int64_t)b * w.dv_sb + (int64_t)kvh * w.dv_sh + (int64_t)key * w.dv_sl + d8 * 8) = vo;
+}
+
 template <int D, int NORM, bool CAP>
 hipError_t launch_d(const BwdArgs& w, hipStream_t stream) {
   const FwdArgs& a = w.f;
@@ -532,13 +589,17 @@ hipError_t launch_d(const BwdArgs& w, hipStream_t stream) {
       bwd_query_mfma<CQ, NORM, CAP, false><<<dim3((unsigned)gq), dim3(CQ::NT), 0, stream>>>(w);
   }
   const int nkb = (a.Lk + 32 * CK::NW - 1) / (32 * CK::NW);
-  const int64_t gk = (int64_t)nkb * a.B * a.Hkv;
+  const int64_t gk = (int64_t)nkb * a.B * (w.key_split ? a.Hq : a.Hkv);
   if (gk) {
     constexpr int lds = KeyLds<CK>::BYTES;
     const hipError_t e = hipFuncSetAttribute((const void*)bwd_key_mfma<CK, NORM, CAP>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     bwd_key_mfma<CK, NORM, CAP><<<dim3((unsigned)gk), dim3(CK::NT), lds, stream>>>(w);
+    if (w.key_split) {
+      const int64_t n8 = (int64_t)a.B * a.Hkv * a.Lk * (D / 8);
+      bwd_kv_reduce<D><<<dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream>>>(w);
+    }
   }
   return hipGetLastError();
 }
@@ -556,6 +617,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 size_t bwd_mfma_rec_bytes(const FwdArgs& a) {
   return (size_t)a.B * a.Hq * rec_blocks(a.Lq) * 3 * kRecRows * sizeof(float);
+}
+
+bool bwd_key_split(const FwdArgs& a) {
+  const int64_t nkb = (a.Lk + 127) / 128;
+  return a.G > 1 && nkb * a.B * a.Hkv < 1024;
+}
+
+size_t bwd_mfma_part_bytes(const FwdArgs& a) {
+  return bwd_key_split(a) ? (size_t)2 * a.B * a.Hq * a.Lk * a.D * sizeof(float) : 0;
 }
 
 bool bwd_mfma_supported(const BwdArgs& w) {
@@ -579,8 +649,9 @@ bool bwd_mfma_supported(const BwdArgs& w) {
   if ((int64_t)a.Lq * a.q_sl * 2 >= lim || (int64_t)a.Lq * w.do_sl * 2 >= lim) return false;
   if ((int64_t)bwd_mfma_rec_bytes(a) >= lim) return false;
   const int64_t gq = (int64_t)((a.Lq + 127) / 128) * a.B * a.Hq;
-  const int64_t gk = (int64_t)((a.Lk + 127) / 128) * a.B * a.Hkv;
-  return gq <= INT32_MAX && gk <= INT32_MAX;
+  const int64_t gk = (int64_t)((a.Lk + 127) / 128) * a.B * a.Hq;
+  const int64_t gr = ((int64_t)a.B * a.Hkv * a.Lk * (a.D / 8) + 255) / 256;
+  return gq <= INT32_MAX && gk <= INT32_MAX && gr <= INT32_MAX;
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& w, hipStream_t stream) {

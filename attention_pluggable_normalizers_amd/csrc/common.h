@@ -149,6 +149,8 @@ struct BwdArgs {
   float* rec;    // workspace: per-row records of the matrix-core kernels
   size_t rec_bytes;
   int have_out;  // f.out / f.o_* hold the forward's output
+  float* part;   // workspace: fp32 partial dK then dV per query head [B, Hq, Lk, D]
+  int key_split; // key kernel: one query head per workgroup, partials in `part`
 };
 
 // Launchers, one per kernel family (defined in their own translation units).
@@ -158,6 +160,8 @@ hipError_t launch_prefill_mfma(const FwdArgs& a, hipStream_t stream);
 // (row constants, records, dQ) then key kernel (dK, dV).
 bool bwd_mfma_supported(const BwdArgs& w);
 size_t bwd_mfma_rec_bytes(const FwdArgs& a);
+size_t bwd_mfma_part_bytes(const FwdArgs& a);
+bool bwd_key_split(const FwdArgs& a);
 hipError_t launch_bwd_mfma(const BwdArgs& w, hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, void* workspace, hipStream_t stream);
 size_t decode_workspace_bytes(const FwdArgs& a);

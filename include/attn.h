@@ -247,7 +247,10 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  * operands, fp32 accumulation); everything else on per-row fp32 kernels.
  * Every output is written in full.  workspace: attn_bwd_workspace_bytes
  * (the larger of 8 bytes per query row, and 768 bytes per 64 query rows of
- * each (batch, head) plus 4 bytes per query row).  Errors as attn_fwd.    */
+ * each (batch, head) plus 4 bytes per query row, rounded up to 256 bytes,
+ * plus, with grouped-query heads and fewer than 1024 blocks of 128 keys
+ * over (batch, kv head), 8 bytes per (batch, query head, key, dim)).
+ * Errors as attn_fwd.                                                     */
 int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
              const attn_tensor* out, const attn_tensor* dout, const float* row_stats,
              const attn_params* p,

@@ -119,3 +119,11 @@ def test_with_forward_output(norm, D, causal, window, cap):
 def test_with_forward_output_sinks():
     _check("softmax1", torch.bfloat16, 64, True, 0, 0.0, 303, sinks=[0.5, -1.0, 2.0, 0.0],
            use_out=True)
+
+
+@pytest.mark.parametrize("norm,D", [("softmax", 64), ("entmax15", 64), ("softmax1", 128)])
+def test_mfma_key_kernel_per_kv_head(norm, D):
+    # 128 x 8 (batch, kv head) pairs of one 128-key block: a grid large enough
+    # that the key kernel keeps one workgroup per kv head and loops over its
+    # G = 2 query heads (smaller grids split the heads and add fp32 partials)
+    _check(norm, torch.bfloat16, D, True, 0, 0.0, 700 + D, shape=(128, 16, 8, 16, 128))
