@@ -901,6 +901,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   };
   bool ovf = !row_ok;         // row left to the extra passes (or no row at all)
   bool settled = false;       // floor has reached the exact threshold of the keys seen once
+  // refloor steps are taken at most kMaxRefloors times per wave in pass A:
+  // where most rows outgrow their buffers (large supports) every row's
+  // overflow would otherwise re-run them for the whole wave, while the
+  // extra passes finish such rows exactly anyway
+  constexpr int kMaxRefloors = 4;
+  int nrefloor = 0;
 
   // The kTop largest lane-block maxima of z this lane has seen, descending.
   // Each is the z of one key, so the threshold of the row's 2 kTop such
@@ -1104,7 +1110,8 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
                 compact_buf<false>(buf, kbuf, cnt, floor_v);
               na = count();
               // ... and, if that is not enough, step the floors on the buffers
-              if (__any(!ovf && cnt + na > cap)) {
+              if (nrefloor < kMaxRefloors && __any(!ovf && cnt + na > cap)) {
+                ++nrefloor;
                 refloor();
                 na = count();
               }
