@@ -1,4 +1,4 @@
-// Matrix-core backward for bf16 inputs with head dim 64 or 128 ("HF Attention
+// Matrix-core backward for bf16 inputs with head dim 64, 128 or 256 ("HF Attention
 // Normalizers", "Important Limitations": the fused kernels save the row max
 // and denominator, or one threshold per query row, and recompute the weights
 // tile by tile in the backward).  Two kernels, the flash-attention-2 split:
@@ -39,10 +39,10 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRecRows = 64;  // rows per block of the record workspace
+constexpr int kRecRows = 32;  // rows per block of the record workspace
 
-// Record workspace: per (batch, query head), blocks of 64 rows, each
-// [3][64] floats: field 0 softmax family m log2(e), sparse tau; field 1
+// Record workspace: per (batch, query head), blocks of 32 rows, each
+// [3][32] floats: field 0 softmax family m log2(e), sparse tau; field 1
 // softmax family 1 / l (0 for a row without keys); field 2 the row constant c.
 __device__ __host__ __forceinline__ int64_t rec_blocks(int Lq) { return (Lq + kRecRows - 1) / kRecRows; }
 __device__ __forceinline__ int64_t rec_offset(int64_t bh, int Lq, int i) {
@@ -164,8 +164,9 @@ __device__ __forceinline__ void elem(float raw, float r0, float r1, const ElemCo
 
 // ---------------------------------------------------------------------------
 // query kernel
+// D = 256: Q, dO and the dQ accumulators need one wave per SIMD
 template <class C, int NORM, bool CAP, bool OUT>
-__global__ __launch_bounds__(C::NT, 2) void bwd_query_mfma(BwdArgs w) {
+__global__ __launch_bounds__(C::NT, C::D == 256 ? 1 : 2) void bwd_query_mfma(BwdArgs w) {
   static_assert(!OUT || NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1, "dO . O is the softmax-family constant");
   const FwdArgs& a = w.f;
   constexpr int KT = C::BN * C::D;
@@ -345,8 +346,9 @@ __global__ __launch_bounds__(C::NT, 2) void bwd_query_mfma(BwdArgs w) {
 }
 
 // ---------------------------------------------------------------------------
-// key kernel: C describes the streamed query tiles (BN = 64 query rows).
-// Dynamic LDS: two stages of (Q tile, dO tile, one record block per wave).
+// key kernel: C describes the streamed query tiles (BN = 32 or 64 query rows,
+// one or two record blocks).  Dynamic LDS: two stages of (Q tile, dO tile,
+// the tile's record blocks per wave).
 template <class C>
 struct KeyLds {
   static constexpr int STAGE = 2 * C::BN * C::D * 2 + C::NW * 1024;
@@ -354,10 +356,11 @@ struct KeyLds {
 };
 
 template <class C, int NORM, bool CAP>
-// D = 128: K, V and the dK, dV accumulators need more than the 256 registers
+// D >= 128: K, V and the dK, dV accumulators need more than the 256 registers
 // of two waves per SIMD, so one wave per SIMD (no spills)
-__global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdArgs w) {
-  static_assert(C::BN == kRecRows, "a query tile is one record block");
+__global__ __launch_bounds__(C::NT, C::D >= 128 ? 1 : 2) void bwd_key_mfma(BwdArgs w) {
+  static_assert(C::BN % kRecRows == 0 && C::BN / kRecRows * 3 * kRecRows * 4 <= 1024,
+                "a query tile's record blocks must fit one 1 KB transfer");
   const FwdArgs& a = w.f;
   constexpr int QT = C::BN * C::D;            // elements of one Q (or dO) tile
   constexpr int STAGE = KeyLds<C>::STAGE;
@@ -439,8 +442,8 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
                                 (uint32_t)((int64_t)Lq * w.do_sl * 2));
     dq_.issue(rq, qt_of(stage), qt * C::BN, live);
     dd_.issue(rd, dt_of(stage), qt * C::BN, live);
-    // the record block of (b, h, qt): 768 bytes (the transfer's last 256 are unused)
-    const int64_t blk = ((int64_t)b * a.Hq + h) * rec_blocks(Lq) + qt;
+    // the record blocks of (b, h, qt), contiguous (the transfer's tail is unused)
+    const int64_t blk = ((int64_t)b * a.Hq + h) * rec_blocks(Lq) + (int64_t)qt * (C::BN / kRecRows);
     const uint32_t so = live ? (uint32_t)(blk * (3 * kRecRows) * 4) : 0x80000000u;
     dma16(rr, lds_addr((const bf16_t*)(lds + stage * STAGE + 2 * QT * 2 + wave * 1024)),
           (uint32_t)lane * 16, __builtin_amdgcn_readfirstlane(so));
@@ -477,9 +480,10 @@ __global__ __launch_bounds__(C::NT, C::D == 128 ? 1 : 2) void bwd_key_mfma(BwdAr
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int qi = kb * 32 + 8 * rg + 4 * g;  // tile row of element r = 4 rg
-          const f32x4 m4 = *(const f32x4*)(rl + qi);
-          const f32x4 l4 = *(const f32x4*)(rl + kRecRows + qi);
-          const f32x4 c4 = *(const f32x4*)(rl + 2 * kRecRows + qi);
+          const float* rb = rl + kb * (3 * kRecRows) + 8 * rg + 4 * g;  // its record block (32 rows)
+          const f32x4 m4 = *(const f32x4*)(rb);
+          const f32x4 l4 = *(const f32x4*)(rb + kRecRows);
+          const f32x4 c4 = *(const f32x4*)(rb + 2 * kRecRows);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rg + e;
@@ -577,8 +581,8 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce(BwdArgs w) {
 template <int D, int NORM, bool CAP>
 hipError_t launch_d(const BwdArgs& w, hipStream_t stream) {
   const FwdArgs& a = w.f;
-  using CQ = Cfg<D, (D == 64 ? 64 : 32), 4>;  // query kernel: key tiles
-  using CK = Cfg<D, 64, 4>;                   // key kernel: query tiles
+  using CQ = Cfg<D, (D == 64 ? 64 : 32), 4>;   // query kernel: key tiles
+  using CK = Cfg<D, (D == 256 ? 32 : 64), 4>;  // key kernel: query tiles
   const int nqb = (a.Lq + CQ::BM - 1) / CQ::BM;
   const int64_t gq = (int64_t)nqb * a.B * a.Hq;
   constexpr bool SOFT = NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1;
@@ -608,7 +612,8 @@ template <int NORM>
 hipError_t launch_n(const BwdArgs& w, hipStream_t stream) {
   const bool cap = w.f.softcap > 0.f;
   if (w.f.D == 64) return cap ? launch_d<64, NORM, true>(w, stream) : launch_d<64, NORM, false>(w, stream);
-  return cap ? launch_d<128, NORM, true>(w, stream) : launch_d<128, NORM, false>(w, stream);
+  if (w.f.D == 128) return cap ? launch_d<128, NORM, true>(w, stream) : launch_d<128, NORM, false>(w, stream);
+  return cap ? launch_d<256, NORM, true>(w, stream) : launch_d<256, NORM, false>(w, stream);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -630,7 +635,7 @@ size_t bwd_mfma_part_bytes(const FwdArgs& a) {
 
 bool bwd_mfma_supported(const BwdArgs& w) {
   const FwdArgs& a = w.f;
-  if (a.dtype != ATTN_BF16 || (a.D != 64 && a.D != 128)) return false;
+  if (a.dtype != ATTN_BF16 || (a.D != 64 && a.D != 128 && a.D != 256)) return false;
   if (a.paged || a.cu_q || a.bm_num) return false;
   if (!(a.scaling > 0.f)) return false;
   const void* ptrs[] = {a.q, a.k, a.v, w.dout, w.dq, w.dk, w.dv, w.have_out ? a.out : a.q};

@@ -156,7 +156,7 @@ struct BwdArgs {
 // Launchers, one per kernel family (defined in their own translation units).
 hipError_t launch_generic(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const FwdArgs& a, hipStream_t stream);
-// Matrix-core backward (bf16, D = 64 or 128, contiguous K/V): query kernel
+// Matrix-core backward (bf16, D = 64, 128 or 256, contiguous K/V): query kernel
 // (row constants, records, dQ) then key kernel (dK, dV).
 bool bwd_mfma_supported(const BwdArgs& w);
 size_t bwd_mfma_rec_bytes(const FwdArgs& a);

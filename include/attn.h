@@ -242,11 +242,11 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  *       dimension contiguous, 16-byte aligned).  softmax / softmax1 then take
  *       the row constant of the Jacobian, sum_j p dP = dout . out, from it
  *       and skip one pass over the keys; the sparse normalizers ignore it.
- * Contiguous K/V, no block mask.  bf16 inputs with D = 64 or 128 (16-byte
+ * Contiguous K/V, no block mask.  bf16 inputs with D = 64, 128 or 256 (16-byte
  * aligned, strides multiples of 8 elements) run on the matrix cores (bf16
  * operands, fp32 accumulation); everything else on per-row fp32 kernels.
  * Every output is written in full.  workspace: attn_bwd_workspace_bytes
- * (the larger of 8 bytes per query row, and 768 bytes per 64 query rows of
+ * (the larger of 8 bytes per query row, and 384 bytes per 32 query rows of
  * each (batch, head) plus 4 bytes per query row, rounded up to 256 bytes,
  * plus, with grouped-query heads and fewer than 1024 blocks of 128 keys
  * over (batch, kv head), 8 bytes per (batch, query head, key, dim)).

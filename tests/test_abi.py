@@ -232,10 +232,10 @@ def test_backward_validation(lib):
     n = ctypes.c_size_t(0)
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv),
                                         ctypes.byref(_p()), ctypes.byref(n)) == 0
-    # per-row kernels: 8 bytes per query row; matrix-core kernels: a 768-byte
-    # record per 64 rows of each (batch, head), 4 bytes per row, and (G > 1)
+    # per-row kernels: 8 bytes per query row; matrix-core kernels: a 384-byte
+    # record per 32 rows of each (batch, head), 4 bytes per row, and (G > 1)
     # fp32 partial dK and dV per query head
-    part_off = (2 * 8 * 1 * 768 + 2 * 8 * 64 * 4 + 255) // 256 * 256
+    part_off = (2 * 8 * 2 * 384 + 2 * 8 * 64 * 4 + 255) // 256 * 256
     assert n.value == max(2 * 8 * 64 * 8, part_off + 2 * 2 * 8 * 64 * 64 * 4)
 
     def call(dout=None, dq=None, dk=None, dv=None, stats=0x9000, p=None, dsinks=None, ws=0x9100,

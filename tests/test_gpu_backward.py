@@ -1,7 +1,7 @@
 """GPU parity of the backward (attn_bwd): dq, dk, dv (and softmax1 sink
 gradients) against the float64 backward oracle, from the row statistics the
 GPU forward saved.  f32 and bf16 inputs, GQA, Lq != Lk, causal / window /
-softcap.  bf16 at head dim 64 and 128 runs the matrix-core kernels (several
+softcap.  bf16 at head dim 64, 128 and 256 runs the matrix-core kernels (several
 key and query tiles, ragged ends, rows without keys); other cases the
 per-row kernels.  Sparsemax rows are drawn so that no score lies within 1e-4 of the
 row's threshold (its Jacobian jumps when a key crosses the support edge, so
@@ -87,7 +87,7 @@ def test_softmax1_sink_gradients():
 
 
 @pytest.mark.parametrize("norm", NORMS)
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal,window,cap", [(False, 0, 0.0), (True, 20, 0.0), (True, 0, 5.0),
                                                (True, 150, 30.0)])
 def test_mfma_masks_and_softcap(norm, D, causal, window, cap):
@@ -95,7 +95,7 @@ def test_mfma_masks_and_softcap(norm, D, causal, window, cap):
 
 
 @pytest.mark.parametrize("norm", NORMS)
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("shape", [(1, 4, 1, 200, 333), (1, 2, 2, 300, 300), (2, 2, 1, 150, 100)],
                          ids=["gqa4_lq200_lk333", "mha_300", "lq150_lk100_empty_rows"])
 def test_mfma_multi_tile(norm, D, shape):
@@ -107,7 +107,7 @@ def test_mfma_sink_gradients():
 
 
 @pytest.mark.parametrize("norm", NORMS)
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal,window,cap", [(True, 0, 0.0), (True, 20, 0.0), (True, 0, 5.0)])
 def test_with_forward_output(norm, D, causal, window, cap):
     # softmax family: the row constant from dout . out (one pass fewer);
@@ -121,7 +121,8 @@ def test_with_forward_output_sinks():
            use_out=True)
 
 
-@pytest.mark.parametrize("norm,D", [("softmax", 64), ("entmax15", 64), ("softmax1", 128)])
+@pytest.mark.parametrize("norm,D", [("softmax", 64), ("entmax15", 64), ("softmax1", 128),
+                                    ("entmax15", 256)])
 def test_mfma_key_kernel_per_kv_head(norm, D):
     # 128 x 8 (batch, kv head) pairs of one 128-key block: a grid large enough
     # that the key kernel keeps one workgroup per kv head and loops over its
