@@ -39,6 +39,11 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+template <int N>
+struct Mode {  // a compile-time int carried by an argument's type
+  static constexpr int value = N;
+};
+
 constexpr int kRecRows = 32;  // rows per block of the record workspace
 
 // Record workspace: per (batch, query head), blocks of 32 rows, each
@@ -449,98 +454,119 @@ __global__ __launch_bounds__(C::NT, C::D >= 128 ? 1 : 2) void bwd_key_mfma(BwdAr
           (uint32_t)lane * 16, __builtin_amdgcn_readfirstlane(so));
   };
 
-  f32x16 dk[C::NDB], dv[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = f32x16{};
   TrK<C> tr;
   tr.init(lane);
 
-  issue(0, 0);
-  wait_vmcnt<0>();
-  lds_barrier();
-  for (int u = 0; u < npos; ++u) {
-    const int cur = u & 1;
-    issue(cur ^ 1, u + 1);
-    const int hh = u / ntq;
-    const int qa = (qt0 + u - hh * ntq) * C::BN;  // first query of the tile
-    if (wave_keys && qa < whi && qa + C::BN > wlo) {
-      const bf16_t* ql = qt_of(cur);
-      const bf16_t* dl = dt_of(cur);
-      const float* rl = (const float*)((const char*)rec_lds + cur * STAGE);
-      f32x16 s[C::NKB], dp[C::NKB];
-      qk_tile<C>(ql, kreg, l32, g, s);
-      qk_tile<C>(dl, vreg, l32, g, dp);
-      // every (query, key) pair of the tile is visible unless the tile
-      // reaches past the wave's bounds
-      const bool edge = (qa < ilo_w1) || (qa + C::BN > ihi_w0);
-      bf16x8 pp[2 * C::NKB], pd[2 * C::NKB];
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        float p16[16], d16[16];
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int qi = kb * 32 + 8 * rg + 4 * g;  // tile row of element r = 4 rg
-          const float* rb = rl + kb * (3 * kRecRows) + 8 * rg + 4 * g;  // its record block (32 rows)
-          const f32x4 m4 = *(const f32x4*)(rb);
-          const f32x4 l4 = *(const f32x4*)(rb + kRecRows);
-          const f32x4 c4 = *(const f32x4*)(rb + 2 * kRecRows);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            const int i = qa + qi + e;
-            const float okf = (!edge || (i >= ilo && i < ihi)) ? 1.f : 0.f;
-            float p, wt, dsdraw;
-            elem<NORM, CAP>(s[kb][r], m4[e], l4[e], ek, p, wt, dsdraw);
-            p16[r] = okf * p;
-            d16[r] = okf * (wt * (dp[kb][r] - c4[e]) * dsdraw);
-          }
-        }
-        pp[2 * kb] = p_operand(p16);
-        pp[2 * kb + 1] = p_operand(p16 + 8);
-        pd[2 * kb] = p_operand(d16);
-        pd[2 * kb + 1] = p_operand(d16 + 8);
-      }
+  // one gradient (dK or dV) of this lane's key: fp32 partial of this query
+  // head ([B, Hq, Lk, D] for dK, then for dV) or the bf16 result
+  auto store = [&](const f32x16* acc, bool is_v) __attribute__((always_inline)) {
+    if (!key_ok) return;
+    if (split) {
+      const int64_t half = (int64_t)a.B * a.Hq * Lk * C::D;
+      const int64_t prow = (is_v ? half : 0) + (((int64_t)b * a.Hq + h0) * Lk + myk) * C::D;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-        for (int t = 0; t < 2 * C::NKB; ++t) {
-          dv[db] = mfma(tr.read(dl, t, db), pp[t], dv[db]);
-          dk[db] = mfma(tr.read(ql, t, db), pd[t], dk[db]);
+        for (int rq = 0; rq < 4; ++rq)
+          *(f32x4*)(w.part + prow + db * 32 + 8 * rq + 4 * g) =
+              f32x4{acc[db][4 * rq], acc[db][4 * rq + 1], acc[db][4 * rq + 2], acc[db][4 * rq + 3]};
+    } else {
+      bf16_t* row = is_v ? (bf16_t*)w.dv + (int64_t)b * w.dv_sb + (int64_t)kvh * w.dv_sh + (int64_t)myk * w.dv_sl
+                         : (bf16_t*)w.dk + (int64_t)b * w.dk_sb + (int64_t)kvh * w.dk_sh + (int64_t)myk * w.dk_sl;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 x4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x4[e] = (bf16_t)acc[db][4 * rq + e];
+          *(bf16x4*)(row + db * 32 + 8 * rq + 4 * g) = x4;
         }
     }
+  };
+
+  // one pass over the positions accumulating dK and / or dV (MODE 0 both,
+  // 1 dV only, 2 dK only; the type of the argument carries MODE)
+  auto run = [&](auto mode_c) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr bool DK = MODE != 1, DV = MODE != 2;
+    f32x16 dk[DK ? C::NDB : 1], dv[DV ? C::NDB : 1];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      if (DK) dk[db] = f32x16{};
+      if (DV) dv[db] = f32x16{};
+    }
+    issue(0, 0);
     wait_vmcnt<0>();
     lds_barrier();
-  }
-  wait_vmcnt<0>();
-  if (key_ok && split) {
-    // fp32 partials of this query head: [B, Hq, Lk, D] for dK, then for dV
-    const int64_t prow = (((int64_t)b * a.Hq + h0) * Lk + myk) * C::D;
-    const int64_t half = (int64_t)a.B * a.Hq * Lk * C::D;
+    for (int u = 0; u < npos; ++u) {
+      const int cur = u & 1;
+      issue(cur ^ 1, u + 1);
+      const int hh = u / ntq;
+      const int qa = (qt0 + u - hh * ntq) * C::BN;  // first query of the tile
+      if (wave_keys && qa < whi && qa + C::BN > wlo) {
+        const bf16_t* ql = qt_of(cur);
+        const bf16_t* dl = dt_of(cur);
+        const float* rl = (const float*)((const char*)rec_lds + cur * STAGE);
+        f32x16 s[C::NKB], dp[DK ? C::NKB : 1];
+        qk_tile<C>(ql, kreg, l32, g, s);
+        if (DK) qk_tile<C>(dl, vreg, l32, g, dp);
+        // every (query, key) pair of the tile is visible unless the tile
+        // reaches past the wave's bounds
+        const bool edge = (qa < ilo_w1) || (qa + C::BN > ihi_w0);
+        bf16x8 pp[2 * C::NKB], pd[2 * C::NKB];
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          float p16[16], d16[16];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d = db * 32 + 8 * rq + 4 * g;
-        *(f32x4*)(w.part + prow + d) = f32x4{dk[db][4 * rq], dk[db][4 * rq + 1], dk[db][4 * rq + 2], dk[db][4 * rq + 3]};
-        *(f32x4*)(w.part + half + prow + d) =
-            f32x4{dv[db][4 * rq], dv[db][4 * rq + 1], dv[db][4 * rq + 2], dv[db][4 * rq + 3]};
-      }
-  } else if (key_ok) {
-    bf16_t* dkrow = (bf16_t*)w.dk + (int64_t)b * w.dk_sb + (int64_t)kvh * w.dk_sh + (int64_t)myk * w.dk_sl;
-    bf16_t* dvrow = (bf16_t*)w.dv + (int64_t)b * w.dv_sb + (int64_t)kvh * w.dv_sh + (int64_t)myk * w.dv_sl;
+          for (int rg = 0; rg < 4; ++rg) {
+            const int qi = kb * 32 + 8 * rg + 4 * g;  // tile row of element r = 4 rg
+            const float* rb = rl + kb * (3 * kRecRows) + 8 * rg + 4 * g;  // its record block (32 rows)
+            const f32x4 m4 = *(const f32x4*)(rb);
+            const f32x4 l4 = *(const f32x4*)(rb + kRecRows);
+            const f32x4 c4 = *(const f32x4*)(rb + 2 * kRecRows);
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = (bf16_t)dk[db][4 * rq + e];
-          v4[e] = (bf16_t)dv[db][4 * rq + e];
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rg + e;
+              const int i = qa + qi + e;
+              const float okf = (!edge || (i >= ilo && i < ihi)) ? 1.f : 0.f;
+              float p, wt, dsdraw;
+              elem<NORM, CAP>(s[kb][r], m4[e], l4[e], ek, p, wt, dsdraw);
+              p16[r] = okf * p;
+              d16[r] = DK ? okf * (wt * (dp[DK ? kb : 0][r] - c4[e]) * dsdraw) : 0.f;
+            }
+          }
+          if (DV) {
+            pp[2 * kb] = p_operand(p16);
+            pp[2 * kb + 1] = p_operand(p16 + 8);
+          }
+          if (DK) {
+            pd[2 * kb] = p_operand(d16);
+            pd[2 * kb + 1] = p_operand(d16 + 8);
+          }
         }
-        *(bf16x4*)(dkrow + db * 32 + 8 * rq + 4 * g) = k4;
-        *(bf16x4*)(dvrow + db * 32 + 8 * rq + 4 * g) = v4;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int t = 0; t < 2 * C::NKB; ++t) {
+            if (DV) dv[DV ? db : 0] = mfma(tr.read(dl, t, db), pp[t], dv[DV ? db : 0]);
+            if (DK) dk[DK ? db : 0] = mfma(tr.read(ql, t, db), pd[t], dk[DK ? db : 0]);
+          }
       }
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+    wait_vmcnt<0>();
+    if (DK) store(dk, false);
+    if (DV) store(dv, true);
+  };
+  // D = 256: dK and dV together with K and V would not fit the registers;
+  // two passes over the tiles (dV from P, then dK from dS) instead
+  if (C::D == 256) {
+    run(Mode<1>{});
+    run(Mode<2>{});
+  } else {
+    run(Mode<0>{});
   }
 }
 
