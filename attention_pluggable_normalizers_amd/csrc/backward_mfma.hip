@@ -361,9 +361,8 @@ struct KeyLds {
 };
 
 template <class C, int NORM, bool CAP>
-// D >= 128: K, V and the dK, dV accumulators need more than the 256 registers
-// of two waves per SIMD, so one wave per SIMD (no spills)
-__global__ __launch_bounds__(C::NT, C::D >= 128 ? 1 : 2) void bwd_key_mfma(BwdArgs w) {
+// D = 256: one wave per SIMD even with dK and dV in separate passes
+__global__ __launch_bounds__(C::NT, C::D >= 256 ? 1 : 2) void bwd_key_mfma(BwdArgs w) {
   static_assert(C::BN % kRecRows == 0 && C::BN / kRecRows * 3 * kRecRows * 4 <= 1024,
                 "a query tile's record blocks must fit one 1 KB transfer");
   const FwdArgs& a = w.f;
@@ -560,9 +559,10 @@ __global__ __launch_bounds__(C::NT, C::D >= 128 ? 1 : 2) void bwd_key_mfma(BwdAr
     if (DK) store(dk, false);
     if (DV) store(dv, true);
   };
-  // D = 256: dK and dV together with K and V would not fit the registers;
-  // two passes over the tiles (dV from P, then dK from dS) instead
-  if (C::D == 256) {
+  // D >= 128: dK and dV together with K and V do not fit the registers of
+  // two waves per SIMD (D = 128) or of one (D = 256); two passes over the
+  // tiles (dV from P, then dK from dS) instead, a quarter more matrix work
+  if (C::D >= 128) {
     run(Mode<1>{});
     run(Mode<2>{});
   } else {
