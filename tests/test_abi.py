@@ -258,3 +258,8 @@ def test_backward_validation(lib):
     assert r == 3 and "workspace" in d
     r, d = call(out=_t((2, 8, 64, 32)))
     assert r == 1 and "out" in d
+    pb = _p()
+    m = _bm()
+    pb.block_mask = ctypes.pointer(m)
+    r, d = call(p=pb)
+    assert r == 2 and "block mask" in d
