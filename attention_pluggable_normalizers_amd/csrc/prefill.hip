@@ -911,8 +911,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // The kTop largest lane-block maxima of z this lane has seen, descending.
   // Each is the z of one key, so the threshold of the row's 2 kTop such
   // values (both lanes) bounds tau from below -- and tightly, since the
-  // support consists mostly of block maxima.
-  constexpr int kTop = 8;
+  // support consists mostly of block maxima.  Sparsemax supports are
+  // smaller than 1.5-entmax supports of the same scores, so its list is
+  // shorter (cheaper to keep and to merge); a power of two for the merge.
+  constexpr int kTop = NORM == ATTN_SPARSEMAX ? 4 : 8;
   float top[kTop];
 #pragma unroll
   for (int i = 0; i < kTop; ++i) top[i] = -INFINITY;

@@ -44,7 +44,7 @@ extern "C" {
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_E_INVALID = 1,      /* null pointer, shape/stride/param inconsistency          */
-  ATTN_E_UNSUPPORTED = 2,  /* valid request outside what this build implements        */
+  ATTN_E_UNSUPPORTED = 2,  /* valid request outside what this library implements      */
   ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than attn_fwd_workspace_bytes */
   ATTN_E_LAUNCH = 4        /* a HIP kernel launch failed                               */
 } attn_status;
