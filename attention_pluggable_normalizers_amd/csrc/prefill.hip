@@ -890,6 +890,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     floor_v = CAP ? floor_f : raw_floor(floor_f, cz);
   };
   int cnt = 0;                // this lane's candidates
+  float cfloor = -INFINITY;   // floor_v at this lane's last compaction
   bool keyed = SC::KEYS;     // wave-uniform: the buffers carry key indices
   int cap = SC::KEYS ? SC::SCAP_K : SC::SCAP_F;  // wave-uniform: entries per lane
   auto scan = [&](double t, double mref, double& c, double& s1, double& s2, float& mn)
@@ -1106,10 +1107,15 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
                 if (!ovf && tf > floor_) set_floor(tf);
                 dirty = false;
               }
-              if (SC::KEYS && keyed)
-                compact_buf<true>(buf, kbuf, cnt, floor_v);
-              else
-                compact_buf<false>(buf, kbuf, cnt, floor_v);
+              // (a lane whose floor has not moved since its last compaction
+              // holds nothing to drop)
+              if (__any(floor_v != cfloor)) {
+                if (SC::KEYS && keyed)
+                  compact_buf<true>(buf, kbuf, cnt, floor_v);
+                else
+                  compact_buf<false>(buf, kbuf, cnt, floor_v);
+                cfloor = floor_v;
+              }
               na = count();
               // ... and, if that is not enough, step the floors on the buffers
               if (nrefloor < kMaxRefloors && __any(!ovf && cnt + na > cap)) {
