@@ -513,10 +513,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
 // (the first SCAP_K values stay where they are).
 //
 // Key indices (KEYS) are kept, with two K stages in pass A to leave room for
-// them, for sparsemax and for 1.5-entmax at D >= 128.  At D = 64 entmax's
-// first floor (z max - 1, i.e. two score units) admits several times its
-// support, and with keys its buffers overflow into compaction that costs
-// more than the gather saves; it keeps three stages and values only.
+// them.  Where the running floors of pass A admit several times the support
+// (broad scores: a fresh row's first floor, z max - 1, lies far below tau)
+// the lookahead after the first tile starts the floors at their final
+// values, so the keyed buffers do not overflow.
 // The extra passes always stream K through NX = 3 stages: once a row is in
 // them its wave has dropped the keys (the output runs on the matrix cores),
 // so the candidate regions move behind the third stage (WREG_X, SCAP_X).
@@ -527,7 +527,7 @@ struct Stages {
 
 template <class C, int NORM>
 struct SparseCfg {
-  static constexpr bool KEYS = NORM == ATTN_SPARSEMAX || C::D >= 128;
+  static constexpr bool KEYS = true;               // candidates carry key indices at first
   static constexpr int LDS_BYTES = C::D == 256 ? 160 * 1024 : 80 * 1024;
   static constexpr int NA = KEYS ? 2 : 3;          // K tiles in flight, threshold passes
   static constexpr int NX = 3;                     // K tiles in flight, extra passes
@@ -907,6 +907,8 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // overflow would otherwise re-run them for the whole wave, while the
   // extra passes finish such rows exactly anyway
   constexpr int kMaxRefloors = 4;
+  // longest key range (per workgroup) that takes the lookahead below
+  constexpr int kLookaheadKeys = 8192;
   int nrefloor = 0;
 
   // The kTop largest lane-block maxima of z this lane has seen, descending.
@@ -1052,6 +1054,84 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   constexpr Stages<SC::NX> sx{};
   k_prologue(sa);
   int cur = 0;
+  if (ts.n > 1 && ts.n * C::BN <= kLookaheadKeys) {
+    // Lookahead.  The first tile is scored for block maxima, and the
+    // workgroup votes on whether its rows would crowd their buffers: some
+    // lane has more than a quarter of its capacity in values above the first
+    // floor the candidate pass would use (the tile's row max - 1).  If so,
+    // the remaining tiles are scored for block maxima too, so that row
+    // maxima and lists of block maxima cover every key and the candidate
+    // pass starts from floors at their final values: far fewer candidates,
+    // rows stay in their keyed buffers and the output is gathered.  Peaked
+    // scores fail the vote; on longer key ranges the running floors settle
+    // early anyway and the extra scoring pass would cost more than it saves.
+    // Either way the lists are emptied afterwards (the candidate pass lists
+    // each block once more) and the K stream restarts at the first tile.
+    float mlook = -INFINITY;
+    bool go = false;
+    for (int p = 0; p < ts.n; ++p) {
+      const bf16_t* kl = ka_of(cur);
+      k_next(sa, p, cur);
+      const int t = ts.tile(p);
+      const int k0 = t * C::BN;
+      f32x16 s[C::NKB];
+      const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo;
+      if (active) {
+        qk_tile<C>(kl, qreg, l32, g, s);
+        if ((k0 + C::BN > wfirst.hi) || (k0 < wlast.lo))
+          mask_tile<C>(s, k0 + 4 * g - mine.lo, mine.hi - mine.lo);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          const float z = block_zmax<CAP>(s[kb], cz, sc_over_cap, capz);
+          mlook = fmaxf(mlook, z);
+          if (z > top[kTop - 1]) push_top(z);
+        }
+      }
+      if (p == 0) {
+        // values of the first tile above its row max - 1
+        const float m0 = pair_max(mlook);
+        const double f0 = (double)m0 - 1.0;
+        int n0 = 0;
+        if (active) {
+          const float f0v = CAP ? float_floor(f0) : raw_floor(float_floor(f0), cz);
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float v = CAP ? zval<true>(s[kb][r], cz, sc_over_cap, capz) : s[kb][r];
+              n0 += v > f0v ? 1 : 0;
+            }
+        }
+        // workgroup vote through a word of the stage that held tile 0,
+        // idle until the transfer issued at the next step
+        k_done(sa, cur);
+        int* const vote = (int*)ka_of(cur == 0 ? NA - 1 : cur - 1);
+        if (tid == 0) *(volatile int*)vote = 0;
+        wait_lgkm0();
+        lds_barrier();
+        if (row_ok && n0 * 4 > cap) *(volatile int*)vote = 1;
+        wait_lgkm0();
+        lds_barrier();
+        go = *(volatile int*)vote != 0;
+        wait_lgkm0();
+        lds_barrier();
+        if (!go) break;
+      } else {
+        k_done(sa, cur);
+      }
+    }
+    wait_vmcnt<0>();
+    if (go) {
+      mrun = pair_max(mlook);
+      const double fl = fmax((double)mrun - 1.0, top_floor());
+      if (!ovf && fl > floor_) set_floor(fl);
+    }
+#pragma unroll
+    for (int i = 0; i < kTop; ++i) top[i] = -INFINITY;
+    // every wave is past the last barrier: no stage is being read
+    k_prologue(sa);
+    cur = 0;
+  }
   for (int u = 0; u < ts.n; ++u) {
     const bf16_t* kl = ka_of(cur);
     k_next(sa, u, cur);

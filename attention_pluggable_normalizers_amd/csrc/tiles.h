@@ -211,6 +211,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Waits for this wave's LDS accesses only (lgkmcnt 0; vmcnt and expcnt at
+// their maxima, so transfers in flight are not waited for).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Workgroup barrier without the release/acquire fences of __syncthreads()
 // (which would wait for every transfer in flight); LDS hazards are covered by
 // explicit vmcnt waits and by each wave consuming its LDS reads before it.
