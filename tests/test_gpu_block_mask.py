@@ -77,6 +77,20 @@ def test_matrix_core_path(norm, D, bk, causal, Hm):
     _check(q, k, v, norm, causal, (num, idx, 128, bk), 1.0 / math.sqrt(D), f"mfma D{D} bk{bk}")
 
 
+@pytest.mark.parametrize("norm", ("sparsemax", "entmax15"))
+def test_matrix_core_path_broad_scores(norm):
+    # flat scores: the sparse kernel scores the listed tiles for block maxima
+    # before collecting candidates
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, Lq, Lk, D = 1, 4, 2, 600, 700, 64
+    g = torch.Generator().manual_seed(55)
+    q = (0.5 * torch.randn(B, Hq, Lq, D, generator=g)).to(torch.bfloat16)
+    k = (0.5 * torch.randn(B, Hkv, Lk, D, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, Lk, D, generator=g).to(torch.bfloat16)
+    num, idx = _lists(rng, B, 1, math.ceil(Lq / 128), math.ceil(Lk / 64), 0.6)
+    _check(q, k, v, norm, True, (num, idx, 128, 64), 1.0 / math.sqrt(D), "broad scores")
+
+
 @pytest.mark.parametrize("norm", NORMS)
 def test_ignored_entries(norm):
     # repeated, descending and out-of-range entries are skipped like the oracle does

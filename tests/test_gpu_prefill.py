@@ -55,6 +55,22 @@ def test_sigma_sweep_reduced(norm):
         check_full(q, k, v, norm, True, 0, 0.0, 1.0 / math.sqrt(128), where=f"sigma{sigma}")
 
 
+@pytest.mark.parametrize("norm", ("sparsemax", "entmax15"))
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("sigma", [0.4, 2.0])
+def test_broad_and_peaked_scores(norm, D, sigma):
+    # broad scores crowd the candidate buffers after the first key tile (the
+    # workgroup then scores every tile for block maxima before collecting
+    # candidates), peaked ones do not; several tiles, ragged ends, causal
+    # and a window
+    q = _rand((1, 4, 333, D), 60 + D, sigma)
+    k = _rand((1, 2, 421, D), 61 + D, sigma)
+    v = _rand((1, 2, 421, D), 62 + D)
+    for window in (0, 150):
+        check_full(q, k, v, norm, True, window, 0.0, 1.0 / math.sqrt(D),
+                   where=f"sigma{sigma} D{D} window{window}")
+
+
 def _sample_rows(cfg, n_random, seed):
     rng = np.random.default_rng(seed)
     rows = set()
