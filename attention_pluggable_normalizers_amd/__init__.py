@@ -11,10 +11,13 @@ from .binding import (
     ATTN_E_WORKSPACE,
     ATTN_OK,
     NORMALIZER_IDS,
+    PATH_NAMES,
     AttnError,
     attn_abi_version,
     attn_bwd,
+    attn_bwd_path,
     attn_fwd,
+    attn_fwd_path,
     attn_fwd_varlen,
     attn_fwd_workspace_bytes,
     attn_last_error_detail,
@@ -30,10 +33,13 @@ __all__ = [
     "ATTN_E_WORKSPACE",
     "ATTN_E_LAUNCH",
     "NORMALIZER_IDS",
+    "PATH_NAMES",
     "AttnError",
     "attn_abi_version",
     "attn_bwd",
+    "attn_bwd_path",
     "attn_fwd",
+    "attn_fwd_path",
     "attn_fwd_varlen",
     "attn_fwd_workspace_bytes",
     "attn_last_error_detail",

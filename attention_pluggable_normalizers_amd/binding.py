@@ -16,6 +16,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_LAUNCH = range(5)
+# attn_path values (include/attn.h) by name
+PATH_NAMES = {0: "none", 1: "prefill_mfma", 2: "decode_split", 3: "per_row", 4: "bwd_mfma",
+              5: "bwd_per_row"}
 NORMALIZER_IDS = {"softmax": 0, "softmax1": 1, "sparsemax": 2, "entmax15": 3}
 _DTYPE_IDS = {torch.float32: 0, torch.bfloat16: 1}
 _DTYPE_UNKNOWN = 99
@@ -90,6 +93,15 @@ def load_library(path=None):
     lib.attn_bwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Params),
                                              P(ctypes.c_size_t)]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.attn_fwd_path.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged), P(_Params),
+                                  P(_Tensor), P(ctypes.c_int)]
+    lib.attn_fwd_path.restype = ctypes.c_int
+    lib.attn_fwd_varlen_path.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Varlen),
+                                         P(_Params), P(_Tensor), P(ctypes.c_int)]
+    lib.attn_fwd_varlen_path.restype = ctypes.c_int
+    lib.attn_bwd_path.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor),
+                                  P(_Params), P(_Tensor), P(_Tensor), P(_Tensor), P(ctypes.c_int)]
+    lib.attn_bwd_path.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_error_detail.argtypes = []
@@ -196,6 +208,23 @@ def attn_fwd_workspace_bytes(q, k, v, *, normalizer, causal=False, window=0, sof
     return n.value
 
 
+def attn_fwd_path(q, k, v, out=None, *, normalizer, causal=False, window=0, softcap=0.0,
+                  scaling=None, paged=None, sinks=None, block_mask=None):
+    """Name of the kernel family ``attn_fwd`` takes for these arguments
+    ("prefill_mfma", "decode_split", "per_row" or "none"); nothing runs."""
+    lib = load_library()
+    if out is None:
+        out = q  # same shape, dtype and alignment class as the output attn_fwd allocates
+    pd = _paged_desc(paged)
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
+                block_mask)
+    path = ctypes.c_int(-1)
+    _check(lib.attn_fwd_path(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)),
+                             ctypes.byref(_desc(v)), ctypes.byref(pd) if pd is not None else None,
+                             ctypes.byref(p), ctypes.byref(_desc(out)), ctypes.byref(path)))
+    return PATH_NAMES[path.value]
+
+
 def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, window=0,
              softcap=0.0, scaling=None, paged=None, workspace=None, stream=None, sinks=None,
              block_mask=None):
@@ -279,6 +308,22 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                              None, 0, stream)
     _check(st)
     return out, row_stats
+
+
+def attn_bwd_path(q, k, v, dout, *, normalizer, causal=False, window=0, softcap=0.0,
+                  scaling=None, sinks=None, dq=None, dk=None, dv=None, out=None):
+    """Name of the kernel family ``attn_bwd`` takes ("bwd_mfma", "bwd_per_row"
+    or "none"); gradients default to tensors laid out like q, k, v."""
+    lib = load_library()
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
+    path = ctypes.c_int(-1)
+    od = ctypes.byref(_desc(out)) if out is not None else None
+    _check(lib.attn_bwd_path(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)),
+                             ctypes.byref(_desc(v)), od, ctypes.byref(_desc(dout)),
+                             ctypes.byref(p), ctypes.byref(_desc(q if dq is None else dq)),
+                             ctypes.byref(_desc(k if dk is None else dk)),
+                             ctypes.byref(_desc(v if dv is None else dv)), ctypes.byref(path)))
+    return PATH_NAMES[path.value]
 
 
 def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, softcap=0.0,

@@ -148,6 +148,29 @@ int validate(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   return ATTN_OK;
 }
 
+// attn_fwd's validation plus the packed-batch descriptor of attn_fwd_varlen.
+int validate_varlen(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                    const attn_varlen* varlen, const attn_params* p, const attn_tensor* out,
+                    float* row_stats, FwdArgs* a) {
+  int st = validate(q, k, v, nullptr, p, out, row_stats, a, true);
+  if (st) return st;
+  if (!varlen) return fail(ATTN_E_INVALID, "varlen descriptor is NULL");
+  if (a->bm_num) return fail(ATTN_E_UNSUPPORTED, "block masks apply to a padded batch only");
+  if (q->shape[0] != 1 || k->shape[0] != 1)
+    return fail(ATTN_E_INVALID, "packed q, k, v must have batch extent 1");
+  if (varlen->num_seqs < 0 || varlen->max_seqlen_q < 0)
+    return fail(ATTN_E_INVALID, "num_seqs and max_seqlen_q must be >= 0");
+  if (varlen->num_seqs > 0 && (!varlen->cu_seqlens_q || !varlen->cu_seqlens_k))
+    return fail(ATTN_E_INVALID, "cu_seqlens_q or cu_seqlens_k is NULL");
+  if ((int64_t)varlen->num_seqs * a->Hq * varlen->max_seqlen_q > (int64_t)INT32_MAX)
+    return fail(ATTN_E_UNSUPPORTED, "too many query rows");
+  a->cu_q = varlen->cu_seqlens_q;
+  a->cu_k = varlen->cu_seqlens_k;
+  a->B = varlen->num_seqs;
+  a->max_q = varlen->max_seqlen_q;
+  return ATTN_OK;
+}
+
 enum class Path { kNone, kGeneric, kPrefill, kDecode };
 
 Path select(const FwdArgs& a) {
@@ -206,27 +229,43 @@ extern "C" int attn_fwd_varlen(const attn_tensor* q, const attn_tensor* k, const
   (void)workspace;
   (void)workspace_bytes;
   FwdArgs a;
-  int st = validate(q, k, v, nullptr, p, out, row_stats, &a, true);
+  int st = validate_varlen(q, k, v, varlen, p, out, row_stats, &a);
   if (st) return st;
-  if (!varlen) return fail(ATTN_E_INVALID, "varlen descriptor is NULL");
-  if (a.bm_num) return fail(ATTN_E_UNSUPPORTED, "block masks apply to a padded batch only");
-  if (q->shape[0] != 1 || k->shape[0] != 1)
-    return fail(ATTN_E_INVALID, "packed q, k, v must have batch extent 1");
-  if (varlen->num_seqs < 0 || varlen->max_seqlen_q < 0)
-    return fail(ATTN_E_INVALID, "num_seqs and max_seqlen_q must be >= 0");
-  if (varlen->num_seqs > 0 && (!varlen->cu_seqlens_q || !varlen->cu_seqlens_k))
-    return fail(ATTN_E_INVALID, "cu_seqlens_q or cu_seqlens_k is NULL");
-  if ((int64_t)varlen->num_seqs * a.Hq * varlen->max_seqlen_q > (int64_t)INT32_MAX)
-    return fail(ATTN_E_UNSUPPORTED, "too many query rows");
-  a.cu_q = varlen->cu_seqlens_q;
-  a.cu_k = varlen->cu_seqlens_k;
-  a.B = varlen->num_seqs;
-  a.max_q = varlen->max_seqlen_q;
   if ((int64_t)a.B * a.Hq * a.max_q == 0 || a.Lq == 0) return ATTN_OK;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const hipError_t e = prefill_mfma_supported(a) ? launch_prefill_mfma(a, s) : launch_generic(a, s);
   if (e != hipSuccess) return fail(ATTN_E_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_path(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                             const attn_paged_kv* paged, const attn_params* p,
+                             const attn_tensor* out, int* path) {
+  if (!path) return fail(ATTN_E_INVALID, "path pointer is NULL");
+  FwdArgs a;
+  int st = validate(q, k, v, paged, p, out, nullptr, &a, true);
+  if (st) return st;
+  switch (select(a)) {
+    case Path::kNone: *path = ATTN_PATH_NONE; break;
+    case Path::kPrefill: *path = ATTN_PATH_PREFILL_MFMA; break;
+    case Path::kDecode: *path = ATTN_PATH_DECODE_SPLIT; break;
+    default: *path = ATTN_PATH_PER_ROW; break;
+  }
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_varlen_path(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                    const attn_varlen* varlen, const attn_params* p,
+                                    const attn_tensor* out, int* path) {
+  if (!path) return fail(ATTN_E_INVALID, "path pointer is NULL");
+  FwdArgs a;
+  int st = validate_varlen(q, k, v, varlen, p, out, nullptr, &a);
+  if (st) return st;
+  if ((int64_t)a.B * a.Hq * a.max_q == 0 || a.Lq == 0)
+    *path = ATTN_PATH_NONE;
+  else
+    *path = prefill_mfma_supported(a) ? ATTN_PATH_PREFILL_MFMA : ATTN_PATH_PER_ROW;
   return ATTN_OK;
 }
 

@@ -398,6 +398,21 @@ extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_t
   return ATTN_OK;
 }
 
+extern "C" int attn_bwd_path(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                             const attn_tensor* out, const attn_tensor* dout, const attn_params* p,
+                             const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
+                             int* path) {
+  if (!path) return bwd_fail(ATTN_E_INVALID, "path pointer is NULL");
+  BwdArgs w;
+  int st = bwd_prepare(q, k, v, out, dout, nullptr, p, dq, dk, dv, &w, false);
+  if (st) return st;
+  if ((int64_t)w.f.B * w.f.Hq * w.f.Lq == 0 && (int64_t)w.f.B * w.f.Hkv * w.f.Lk == 0)
+    *path = ATTN_PATH_NONE;
+  else
+    *path = bwd_mfma_supported(w) ? ATTN_PATH_BWD_MFMA : ATTN_PATH_BWD_PER_ROW;
+  return ATTN_OK;
+}
+
 extern "C" int attn_bwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
                                         const attn_tensor* v, const attn_params* p, size_t* bytes) {
   if (!bytes) return bwd_fail(ATTN_E_INVALID, "bytes is NULL");

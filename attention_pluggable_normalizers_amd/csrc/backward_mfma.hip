@@ -148,8 +148,13 @@ __device__ __forceinline__ void elem(float raw, float r0, float r1, const ElemCo
   float z;
   if (CAP) {
     const float y = raw * k.sc_over_cap;
-    const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);  // exp(2y)
-    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);  // tanh(y)
+    float t;
+    if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1) {
+      const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);  // exp(2y)
+      t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);            // tanh(y)
+    } else {
+      t = tanhf(y);  // the forward's sparse z (same support)
+    }
     z = k.capz * t;
     dsdraw = k.scaling * (1.f - t * t);
   } else {

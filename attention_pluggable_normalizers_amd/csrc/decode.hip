@@ -129,15 +129,42 @@ __device__ __forceinline__ SparseLists sparse_lists(float* ws, const FwdArgs& a,
 constexpr int kZPad = kSplit + 32;  // LDS row of a split's z values (chunk overhang included)
 constexpr int kFloorSteps = 3;      // threshold steps on a split's own keys
 
+// Rounding margin of a split floor (z units).  The floor steps run in fp64
+// over at most kSplit keys whose y = z - mh lie in (-1, 0]: y and y^2 are
+// exact in fp64, and each of the sums c, s1 = sum y, s2 = sum y^2 is off by
+// at most kSplit * 2^-53 * kSplit < 3e-11.  The sparsemax step (s1 - 1) / c
+// and the 1.5-entmax Newton step (f / f' with f' = 2 sum (z - t) >= 2 while
+// f > 0) inherit errors of the same order; the 1.5-entmax closed form
+// mu - sqrt(delta) is the worst conditioned: delta = (1 - ss) / c carries an
+// error e of at most ~1e-13, which moves sqrt(delta) by at most sqrt(e) <
+// 4e-7.  The jump of a step to the set's minimum is taken only when the
+// closed form is inconsistent, and lands at most as far above tau as that
+// closed form's own error.  So every computed step stays below the split's
+// exact threshold plus 5e-7; the floor subtracts 1e-6 (and the rounding of
+// mh + y, 2^-40 |mh|), then rounds towards -inf to a float.
+__device__ __forceinline__ double floor_margin(float mh) { return 1e-6 + 0x1p-40 * fabs((double)mh); }
+
+// Largest float not above x.
+__device__ __forceinline__ float float_below(double x) {
+  float f = (float)x;
+  if ((double)f > x) {  // step one ulp towards -inf
+    unsigned u = __float_as_uint(f);
+    u = f > 0.f ? u - 1u : (f < 0.f ? u + 1u : 0x80000001u);
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+
 // End of a sparse split.  The heads of the group run side by side (64 / GP
 // lanes each, GP = G rounded up to a power of two): per head the split max
-// mh, up to kFloorSteps threshold steps in fp32 over the split's own keys
-// starting at mh - 1 (the same step as the row solver: the closed form over
-// {z > t} if it lies below that set's minimum, else a larger lower bound),
-// then the floor, lowered by a margin that covers the fp32 rounding of the
-// steps, and the keys above it compacted in key order with ballots.
-// zs[h][key - s kSplit] holds z of the split's keys [k_begin, k_end); mx is
-// the lane's running max of its head (lane % 16); one wave.
+// mh, up to kFloorSteps threshold steps in fp64 over the split's own keys
+// starting at mh - 1 (the row solver's step: the closed form over {z > t} if
+// it lies below that set's minimum, else a larger lower bound).  The
+// threshold of a subset of a row's keys never exceeds the row's, so every
+// step is a lower bound on tau; the floor is the last one minus the rounding
+// margin above, and the keys above it are compacted in key order with
+// ballots.  zs[h][key - s kSplit] holds z of the split's keys [k_begin,
+// k_end); mx is the lane's running max of its head (lane % 16); one wave.
 template <int NORM, int GM>
 __device__ __forceinline__ void sparse_split_lists(const FwdArgs& a, float* ws, int ns, int b, int kvh,
                                                    int s, int k_begin, int k_end, float mx,
@@ -155,18 +182,20 @@ __device__ __forceinline__ void sparse_split_lists(const FwdArgs& a, float* ws, 
   const bool act = h < G;
   const int hr = act ? h : 0;
   const float mh = __shfl(mx, hr, 64);     // lane h holds head h's max
-  float t = mh - 1.0f;
+  const double mref = (double)mh;
+  double t = mref - 1.0;
   bool done = false;
   for (int it = 0; it < kFloorSteps; ++it) {
-    float c = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
+    double c = 0.0, s1 = 0.0, s2 = 0.0;
+    float mn = INFINITY;
     if (!done) {
       for (int idx = lo + sub; idx < hi; idx += lph) {
         const float v = zs[hr][idx];
-        if (v > t) {
-          const float y = v - mh;
-          c += 1.f;
+        if ((double)v > t) {
+          const double y = (double)v - mref;
+          c += 1.0;
           s1 += y;
-          s2 = fmaf(y, y, s2);
+          s2 += y * y;
           mn = fminf(mn, v);
         }
       }
@@ -177,33 +206,14 @@ __device__ __forceinline__ void sparse_split_lists(const FwdArgs& a, float* ws, 
       s2 += __shfl_xor(s2, o, 64);
       mn = fminf(mn, __shfl_xor(mn, o, 64));
     }
-    if (!done && c > 0.f) {
-      float tcf, step;
-      bool valid;
-      if (NORM == ATTN_SPARSEMAX) {
-        tcf = (s1 - 1.f) / c;
-        valid = true;
-        step = tcf;
-      } else {
-        const float mu = s1 / c;
-        const float delta = (1.f - (s2 - s1 * mu)) / c;
-        valid = delta >= 0.f;
-        tcf = valid ? mu - sqrtf(delta) : 0.f;
-        const float ty = t - mh;
-        const float f = s2 - 2.f * ty * s1 + c * ty * ty - 1.f;
-        const float fp = 2.f * (s1 - c * ty);
-        step = ty + f / fp;
-      }
-      const float mny = mn - mh;
-      if (valid && tcf < mny) {
-        t = mh + tcf;
-        done = true;
-      } else {
-        t = fmaxf(t, mh + fmaxf(step, mny));
-      }
+    if (!done && c > 0.0) {
+      bool ex;
+      const double tn = solve_step<NORM>(c, s1, s2, mn, mref, t, ex);
+      done = ex;
+      t = ex ? tn : fmax(t, tn);
     }
   }
-  const float tf = t - (1e-2f + 1e-5f * fabsf(mh));  // fp32 rounding margin
+  const float tf = mh == -INFINITY ? -INFINITY : float_below(t - floor_margin(mh));
   // compact in LDS, in place (an entry moves to a position at or below the
   // one it was read from, and every read of a round precedes its writes),
   // then copy the list out with contiguous stores
@@ -327,9 +337,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
         float v = sacc[sb][r];
         if (NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15) {
           if (CAP) {
-            const float y = v * sc_over_cap;
-            const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
-            v = capz * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
+            v = capz * tanhf(v * sc_over_cap);  // accurate near 0 (support test)
           } else {
             v = v * scale;
           }
@@ -578,11 +586,12 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
       for (int r = 0; r < 4; ++r) {
         const int j = k0 + sb * 16 + 4 * (lane >> 4) + r;
         float v = sacc[r];
-        if (CAP) {
+        if (CAP && SPARSE) {
+          v = capz * tanhf(v * sc_over_cap);  // accurate near 0 (support test)
+        } else if (CAP) {
           const float y = v * sc_over_cap;
           const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
-          const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
-          v = SPARSE ? capz * th : a.softcap * kLog2e * th;
+          v = a.softcap * kLog2e * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
         } else {
           v = v * (SPARSE ? scale : c2);
         }
@@ -1011,6 +1020,19 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, flo
       break;
     }
     t = fmax(t, tn);
+  }
+  // Every split floor is a provable lower bound on tau (see floor_margin), so
+  // the search ends with an exact closed form at or above t0.  A row for
+  // which it does not (the loop ran out, or tau < t0) cannot come out of the
+  // arithmetic above; it is reported rather than hidden: out and row_stats
+  // are NaN.
+  if (!(tau < INFINITY) || tau < t0) {
+    for (int d = tid; d < D; d += 256) orow[d] = (bf16_t)NAN;
+    if (a.stats && tid == 0) {
+      a.stats[(int64_t)row * 2] = NAN;
+      a.stats[(int64_t)row * 2 + 1] = NAN;
+    }
+    return;
   }
 
   // 4. weighted sum of the support's V rows

@@ -148,14 +148,16 @@ __device__ __forceinline__ float capped_log2(float raw, float sc_over_cap, float
 }
 
 // z of one raw score q.k (the value the threshold acts on).
-// Monotone in raw (cz, capz > 0); a masked score (-inf) stays -inf.
+// Monotone in raw (cz, capz > 0); a masked score (-inf) stays -inf.  Under
+// softcap the support test compares z with tau directly, so tanh is the
+// library's (a few ulp relative error at every argument), not the
+// 1 - 2 / (1 + e^2y) form of the softmax path, which loses relative accuracy
+// near 0 (about 2e-7 absolute, i.e. 1e-5 in z at cap 50).
 template <bool CAP>
 __device__ __forceinline__ float zval(float raw, float cz, float sc_over_cap, float capz) {
 #pragma clang fp contract(off)
   if (CAP) {
-    const float y = raw * sc_over_cap;
-    const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * y);
-    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
+    const float t = tanhf(raw * sc_over_cap);
     return raw == -INFINITY ? -INFINITY : capz * t;
   }
   return raw * cz;

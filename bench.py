@@ -17,7 +17,11 @@ with --no-decode) and the fp64 CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
        [--no-extra] [--no-cpu-baseline]
-Prints one JSON line.
+       python bench.py --kernel WORKLOAD:NORMALIZER [--steps K] [--warmup W]
+Prints one JSON line.  --kernel launches one kernel configuration only (for
+profiler runs): WORKLOAD is one of llama, qwen0.5, qwen1, qwen2, gemma,
+decode, chunk (chunked prefill over the decode cache, 512 queries per
+sequence).
 """
 
 import argparse
@@ -244,6 +248,63 @@ def chunk_bench(apn, x, dcfg, lens, paged, dev, Lq, reps=5):
     return {"Lq": Lq, "credited_flop_per_launch": flops, "per_normalizer": per}
 
 
+KERNEL_WORKLOADS = ("llama", "qwen0.5", "qwen1", "qwen2", "gemma", "decode", "chunk")
+
+
+def kernel_only(apn, W, dev, spec, steps, warmup):
+    """Launch one workload / normalizer pair `warmup` + `steps` times (for
+    profiler runs) and return its median launch time and credited rate."""
+    import torch
+    name, _, norm = spec.partition(":")
+    if name not in KERNEL_WORKLOADS or norm not in W.NORMALIZERS:
+        raise SystemExit(f"--kernel takes WORKLOAD:NORMALIZER with WORKLOAD in {KERNEL_WORKLOADS}"
+                         f" and NORMALIZER in {W.NORMALIZERS}")
+    res = {"kernel": spec, "steps": steps, "warmup": warmup}
+    if name in ("decode", "chunk"):
+        dcfg = W.DECODE
+        x = W.make_paged(dcfg, device=dev)
+        lens = x.seq_lens.cpu().tolist()
+        paged = {"block_table": x.block_table, "seq_lens": x.seq_lens,
+                 "block_size": x.block_size, "max_blocks": x.max_blocks}
+        if name == "decode":
+            q = x.q
+            nbytes = apn.attn_fwd_workspace_bytes(q, x.k_cache, x.v_cache, normalizer=norm,
+                                                  causal=True, scaling=dcfg.scaling, paged=paged)
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        else:
+            g = torch.Generator(device=dev).manual_seed(dcfg.seed + 31)
+            Lq = 512
+            q = torch.randn(dcfg.B, dcfg.Hq, Lq, dcfg.D, generator=g, device=dev).to(torch.bfloat16)
+            ws = None
+            pairs = sum(Lq * (n - Lq) + Lq * (Lq + 1) // 2 if n >= Lq else n * (n + 1) // 2
+                        for n in lens)
+            res["credited_flop_per_launch"] = 4 * dcfg.D * pairs * dcfg.Hq
+        out = torch.empty_like(q)
+        st = torch.empty(*q.shape[:3], 2, dtype=torch.float32, device=dev)
+        f = lambda: apn.attn_fwd(q, x.k_cache, x.v_cache, out, st, normalizer=norm, causal=True,
+                                 scaling=dcfg.scaling, paged=paged, workspace=ws)
+        us = time_launches(f, steps, warmup)
+        if name == "decode":
+            res["bytes_per_launch"] = decode_bytes(x, dcfg, lens, norm, st[..., 1].cpu())
+            res["GB/s"] = round(res["bytes_per_launch"] / (us * 1e-6) / 1e9, 1)
+    else:
+        cfg = {"llama": W.LLAMA, "qwen0.5": W.qwen(0.5), "qwen1": W.qwen(1.0),
+               "qwen2": W.qwen(2.0), "gemma": W.GEMMA}[name]
+        q, k, v = [x.to(dev) for x in W.make_prefill(cfg)]
+        out = torch.empty_like(q)
+        st = torch.empty(*q.shape[:3], 2, dtype=torch.float32, device=dev)
+        f = lambda: apn.attn_fwd(q, k, v, out, st, normalizer=norm, causal=cfg.causal,
+                                 window=cfg.window, softcap=cfg.softcap, scaling=cfg.scaling)
+        us = time_launches(f, steps, warmup)
+        res["credited_flop_per_launch"] = 4 * cfg.D * credited_pairs(cfg)
+    res["us"] = round(us, 1)
+    if "credited_flop_per_launch" in res:
+        tf = res["credited_flop_per_launch"] / (us * 1e-6) / 1e12
+        res["TFLOP/s"] = round(tf, 1)
+        res["pct_bf16_peak"] = round(100 * tf / PEAK_BF16_TFLOPS, 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +316,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a reference for scaling hardware byte counters)")
+    ap.add_argument("--kernel", default="",
+                    help="WORKLOAD:NORMALIZER -- launch only this kernel configuration "
+                         "(warmup + steps launches) and print its median time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this forward has no multi-GPU path "
@@ -267,6 +331,9 @@ def main():
 
     apn.load_library()
     dev = torch.device("cuda:0")
+    if args.kernel:
+        print(json.dumps(kernel_only(apn, W, dev, args.kernel, args.steps, args.warmup)), flush=True)
+        return
     cfg = W.LLAMA
     q, k, v = [x.to(dev) for x in W.make_prefill(cfg)]
     out = torch.empty_like(q)

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 /* Status codes. */
 typedef enum attn_status {
@@ -216,6 +216,37 @@ int attn_fwd_varlen(const attn_tensor* q, const attn_tensor* k, const attn_tenso
                     const attn_tensor* out, float* row_stats,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernel family a call runs on (attn_fwd_path, attn_fwd_varlen_path,
+ * attn_bwd_path).  The selection is a fixed function of dtype, head dim,
+ * layout, alignment and size; it never changes at run time ("HF Attention
+ * Normalizers", "Strict vs Fallback Mode").  The per-row kernels (one wave
+ * per query row, fp32 arithmetic, scores recomputed per pass) are the
+ * correctness path for everything the tiled kernels do not take, one to two
+ * orders of magnitude slower on large bf16 problems.                       */
+typedef enum attn_path {
+  ATTN_PATH_NONE = 0,          /* nothing to compute (an empty extent)          */
+  ATTN_PATH_PREFILL_MFMA = 1,  /* tiled matrix-core prefill kernels             */
+  ATTN_PATH_DECODE_SPLIT = 2,  /* split-KV paged decode kernels                 */
+  ATTN_PATH_PER_ROW = 3,       /* per-row forward kernel                        */
+  ATTN_PATH_BWD_MFMA = 4,      /* matrix-core backward kernels                  */
+  ATTN_PATH_BWD_PER_ROW = 5    /* per-row backward kernels                      */
+} attn_path;
+
+/* attn_fwd_path -- the attn_path that attn_fwd would take for exactly these
+ * arguments (host computation only: nothing is read from or written to
+ * device memory, nothing is enqueued).  Validates like attn_fwd (the data
+ * pointers enter only through their alignment) and writes the path to
+ * *path (host pointer).  Returns ATTN_OK or the error attn_fwd would give
+ * before launching.                                                        */
+int attn_fwd_path(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                  const attn_paged_kv* paged, const attn_params* p,
+                  const attn_tensor* out, int* path);
+
+/* attn_fwd_varlen_path -- the same for attn_fwd_varlen. */
+int attn_fwd_varlen_path(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                         const attn_varlen* varlen, const attn_params* p,
+                         const attn_tensor* out, int* path);
+
 /* attn_fwd_workspace_bytes -- workspace size attn_fwd needs for these
  * arguments (host computation only; no device access).  Validates the same
  * way attn_fwd does and writes the size to *bytes (host pointer).          */
@@ -256,6 +287,14 @@ int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
              const attn_params* p,
              const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
              float* dsinks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_bwd_path -- the attn_path (ATTN_PATH_BWD_MFMA or ATTN_PATH_BWD_PER_ROW,
+ * ATTN_PATH_NONE when there is nothing to compute) that attn_bwd would take
+ * for these arguments; host computation only, as attn_fwd_path.            */
+int attn_bwd_path(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                  const attn_tensor* out, const attn_tensor* dout, const attn_params* p,
+                  const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
+                  int* path);
 
 /* attn_bwd_workspace_bytes -- workspace size attn_bwd needs (host only). */
 int attn_bwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,

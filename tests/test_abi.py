@@ -32,13 +32,14 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_varlen", "attn_fwd_workspace_bytes", "attn_strerror",
                             "attn_last_error_detail", "attn_abi_version", "attn_bwd",
-                            "attn_bwd_workspace_bytes"])
+                            "attn_bwd_workspace_bytes", "attn_fwd_path", "attn_fwd_varlen_path",
+                            "attn_bwd_path"])
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 5
+    assert apn.attn_abi_version() == 6
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -263,3 +264,83 @@ def test_backward_validation(lib):
     pb.block_mask = ctypes.pointer(m)
     r, d = call(p=pb)
     assert r == 2 and "block mask" in d
+
+
+def _fwd_path(lib, q, k, v, p, out=None, paged=None):
+    path = ctypes.c_int(-1)
+    r = lib.attn_fwd_path(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                          ctypes.byref(paged) if paged else None, ctypes.byref(p),
+                          ctypes.byref(out or q), ctypes.byref(path))
+    return r, B.PATH_NAMES.get(path.value)
+
+
+@pytest.mark.parametrize("q,kv,dtype,paged,p,want", [
+    # the five workloads' shapes (bf16, aligned): tiled kernels
+    ((4, 32, 2048, 64), (4, 8, 2048, 64), torch.bfloat16, None, dict(), "prefill_mfma"),
+    ((2, 16, 8192, 128), (2, 8, 8192, 128), torch.bfloat16, None, dict(norm=3), "prefill_mfma"),
+    ((1, 16, 8192, 256), (1, 8, 8192, 256), torch.bfloat16, None,
+     dict(window=4096, softcap=50.0, scaling=0.0625), "prefill_mfma"),
+    ((64, 32, 1, 128), (70000, 16, 8, 128), torch.bfloat16, 16, dict(norm=2), "decode_split"),
+    ((64, 32, 512, 128), (70000, 16, 8, 128), torch.bfloat16, 16, dict(), "prefill_mfma"),
+    # what the per-row kernel takes
+    ((1, 2, 8, 16), (1, 2, 8, 16), torch.float32, None, dict(scaling=0.25), "per_row"),
+    ((1, 4, 100, 64), (1, 2, 100, 64), torch.float32, None, dict(), "per_row"),
+    ((1, 4, 100, 96), (1, 2, 100, 96), torch.bfloat16, None, dict(), "per_row"),
+    ((1, 4, 100, 64), (1, 2, 100, 64), torch.bfloat16, None, dict(scaling=-0.1), "per_row"),
+    ((2, 34, 1, 128), (100, 16, 2, 128), torch.bfloat16, 16, dict(), "per_row"),  # G = 17
+    ((2, 4, 7, 128), (100, 12, 2, 128), torch.bfloat16, 12, dict(), "per_row"),  # pages of 12
+    ((0, 4, 7, 64), (0, 2, 7, 64), torch.bfloat16, None, dict(), "none"),
+])
+def test_fwd_path(lib, q, kv, dtype, paged, p, want):
+    pd = _paged(bs=paged, max_blocks=2048) if paged else None
+    r, path = _fwd_path(lib, _t(q, dtype), _t(kv, dtype), _t(kv, dtype), _p(**p), paged=pd)
+    assert r == 0, apn.attn_last_error_detail()
+    assert path == want
+
+
+def test_fwd_path_unaligned(lib):
+    # a pointer off the 16-byte grid, or a row stride that is not a multiple
+    # of 8 elements, leaves the tiled kernels
+    q = _t((1, 4, 100, 64))
+    kv = _t((1, 2, 100, 64))
+    assert _fwd_path(lib, q, kv, kv, _p())[1] == "prefill_mfma"
+    q.data = 0x1002
+    assert _fwd_path(lib, q, kv, kv, _p())[1] == "per_row"
+    q2 = _t((1, 4, 100, 64), strides=[4 * 100 * 68, 100 * 68, 68, 1])
+    assert _fwd_path(lib, q2, kv, kv, _p())[1] == "per_row"
+    r, _ = _fwd_path(lib, q, kv, kv, _p(norm=9))
+    assert r == 1
+
+
+def test_fwd_varlen_path(lib):
+    q = _t((1, 8, 100, 64))
+    kv = _t((1, 2, 120, 64))
+    vl = B._Varlen()
+    vl.cu_seqlens_q, vl.cu_seqlens_k, vl.num_seqs, vl.max_seqlen_q = 0x5000, 0x6000, 3, 50
+    path = ctypes.c_int(-1)
+    r = lib.attn_fwd_varlen_path(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv),
+                                 ctypes.byref(vl), ctypes.byref(_p()), ctypes.byref(q),
+                                 ctypes.byref(path))
+    assert r == 0 and B.PATH_NAMES[path.value] == "prefill_mfma"
+    qf, kvf = _t((1, 8, 100, 64), torch.float32), _t((1, 2, 120, 64), torch.float32)
+    r = lib.attn_fwd_varlen_path(ctypes.byref(qf), ctypes.byref(kvf), ctypes.byref(kvf),
+                                 ctypes.byref(vl), ctypes.byref(_p()), ctypes.byref(qf),
+                                 ctypes.byref(path))
+    assert r == 0 and B.PATH_NAMES[path.value] == "per_row"
+
+
+def test_bwd_path(lib):
+    def path_of(q, kv, p=None):
+        path = ctypes.c_int(-1)
+        r = lib.attn_bwd_path(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv), None,
+                              ctypes.byref(q), ctypes.byref(p or _p()), ctypes.byref(q),
+                              ctypes.byref(kv), ctypes.byref(kv), ctypes.byref(path))
+        return r, B.PATH_NAMES.get(path.value)
+    assert path_of(_t((4, 32, 2048, 64)), _t((4, 8, 2048, 64))) == (0, "bwd_mfma")
+    assert path_of(_t((1, 4, 64, 96)), _t((1, 2, 64, 96))) == (0, "bwd_per_row")
+    assert path_of(_t((1, 4, 64, 64), torch.float32), _t((1, 2, 64, 64), torch.float32)) == \
+        (0, "bwd_per_row")
+    pb = _p()
+    m = _bm()
+    pb.block_mask = ctypes.pointer(m)
+    assert path_of(_t(Q), _t(KV), pb)[0] == 2
