@@ -116,6 +116,28 @@ __device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
   qb = nqb - 1 - (id - bh * nqb);
 }
 
+// The same XCD-contiguous ranges, ordered longest first across the range:
+// an XCD's workgroups run the last (longest causal) q-block of every head of
+// its range, then the one before, and so on, so its CUs are packed
+// longest-job-first (a per-head order leaves the short blocks of early heads
+// occupying CUs while long blocks of later heads wait).
+__device__ __forceinline__ void block_coords_lpt(int nqb, int& bh, int& qb) {
+  const int nblk = gridDim.x;
+  int id = blockIdx.x;
+  const bool xcd = (nblk & 7) == 0;
+  if (xcd) id = (id & 7) * (nblk >> 3) + (id >> 3);
+  const int per = xcd ? nblk >> 3 : nblk;  // ids per XCD range
+  if (per % nqb == 0) {
+    const int heads = per / nqb;           // whole heads per range
+    const int x = id / per, j = id - x * per;
+    qb = nqb - 1 - j / heads;
+    bh = x * heads + (j - (j / heads) * heads);
+  } else {
+    bh = id / nqb;
+    qb = nqb - 1 - (id - bh * nqb);
+  }
+}
+
 // Max / sum over the two lanes that share a query row (lanes l and l ^ 32):
 // v_permlane32_swap hands each half the other half's value.
 __device__ __forceinline__ float pair_max(float x) {

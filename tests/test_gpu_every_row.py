@@ -48,7 +48,8 @@ def _prefill_every_row(cfg, norm, bh_list):
     torch.cuda.empty_cache()
     jobs = slice_jobs(q.float().numpy(), k.float().numpy(), v.float().numpy(), out_g, st_g, pats,
                       norm, cfg.causal, cfg.window, cfg.softcap, cfg.scaling, "bf16", bh_list,
-                      cfg.Hq // cfg.Hkv, chunk=min(cfg.Lq, 2048), where=cfg.name)
+                      cfg.Hq // cfg.Hkv, chunk=2048 if len(bh_list) > 16 else 512,
+                      where=cfg.name)
     worst, nrows, fails = run_jobs(jobs)
     assert nrows == len(bh_list) * cfg.Lq
     assert not fails, "\n".join(fails[:20])
