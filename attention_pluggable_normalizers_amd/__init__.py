@@ -17,6 +17,7 @@ from .binding import (
     attn_bwd,
     attn_bwd_path,
     attn_fwd,
+    attn_fwd_noalloc,
     attn_fwd_path,
     attn_fwd_varlen,
     attn_fwd_workspace_bytes,
@@ -39,6 +40,7 @@ __all__ = [
     "attn_bwd",
     "attn_bwd_path",
     "attn_fwd",
+    "attn_fwd_noalloc",
     "attn_fwd_path",
     "attn_fwd_varlen",
     "attn_fwd_workspace_bytes",

@@ -93,6 +93,9 @@ def load_library(path=None):
     lib.attn_bwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Params),
                                              P(ctypes.c_size_t)]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.attn_fwd_noalloc.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged), P(_Params),
+                                     P(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_noalloc.restype = ctypes.c_int
     lib.attn_fwd_path.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Paged), P(_Params),
                                   P(_Tensor), P(ctypes.c_int)]
     lib.attn_fwd_path.restype = ctypes.c_int
@@ -264,6 +267,29 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
                       row_stats.data_ptr() if row_stats is not None else None,
                       ws_ptr, ws_len, stream)
     _check(st)
+    return out, row_stats
+
+
+def attn_fwd_noalloc(q, k, v, out, row_stats=None, *, normalizer, causal=False, window=0,
+                     softcap=0.0, scaling=None, paged=None, stream=None, sinks=None,
+                     block_mask=None):
+    """``attn_fwd`` without any device allocation: ``out`` must be given, and
+    the paged-decode workspace is the library's fixed per-GPU scratch (calls
+    that overlap on one GPU race).  Returns ``(out, row_stats)``."""
+    lib = load_library()
+    if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+                                  or tuple(row_stats.shape) != (*q.shape[:3], 2)):
+        raise ValueError("row_stats must be a contiguous float32 tensor [B, Hq, Lq, 2]")
+    pd = _paged_desc(paged)
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
+                block_mask)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib.attn_fwd_noalloc(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)),
+                                ctypes.byref(_desc(v)),
+                                ctypes.byref(pd) if pd is not None else None, ctypes.byref(p),
+                                ctypes.byref(_desc(out)),
+                                row_stats.data_ptr() if row_stats is not None else None, stream))
     return out, row_stats
 
 

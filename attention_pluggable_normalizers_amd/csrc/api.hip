@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace attn {
@@ -216,6 +218,77 @@ extern "C" int attn_fwd(const attn_tensor* q, const attn_tensor* k, const attn_t
   switch (path) {
     case Path::kPrefill: e = launch_prefill_mfma(a, s); break;
     case Path::kDecode: e = launch_decode(a, workspace, s); break;
+    default: e = launch_generic(a, s); break;
+  }
+  if (e != hipSuccess) return fail(ATTN_E_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of attn_fwd: the workspace is a fixed device array
+// of this library (each GPU the library runs on holds its own copy until the
+// process ends).  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is ever passed to a kernel.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device (nullptr: not yet)
+
+// Device address of this device's `scratch` (looked up on the first call on
+// the device, with it current); nullptr with *err set on failure.
+void* scratch_for(int dev, hipError_t* err) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                const attn_paged_kv* paged, const attn_params* p,
+                                const attn_tensor* out, float* row_stats, void* stream) {
+  FwdArgs a;
+  int st = validate(q, k, v, paged, p, out, row_stats, &a, true);
+  if (st) return st;
+  const Path path = select(a);
+  const size_t need = workspace_for(a);
+  if (need > kScratchBytes) {
+    snprintf(g_detail, sizeof(g_detail),
+             "needs %zu bytes of workspace, more than the %zu bytes of the library's fixed "
+             "scratch; call attn_fwd with a workspace",
+             need, kScratchBytes);
+    return ATTN_E_WORKSPACE;
+  }
+  if (path == Path::kNone) return ATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+      return fail(ATTN_E_LAUNCH, "no usable current device for the fixed scratch");
+    ws = scratch_for(dev, &e);
+    if (!ws) return fail(ATTN_E_LAUNCH, "hipGetSymbolAddress of the scratch failed: %s",
+                         hipGetErrorString(e));
+  }
+  hipError_t e;
+  switch (path) {
+    case Path::kPrefill: e = launch_prefill_mfma(a, s); break;
+    case Path::kDecode: e = launch_decode(a, ws, s); break;
     default: e = launch_generic(a, s); break;
   }
   if (e != hipSuccess) return fail(ATTN_E_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));

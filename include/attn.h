@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 /* Status codes. */
 typedef enum attn_status {
@@ -184,6 +184,23 @@ int attn_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
              const attn_paged_kv* paged, const attn_params* p,
              const attn_tensor* out, float* row_stats,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments minus the workspace, the same
+ * kernels and results.  Where attn_fwd needs a workspace (paged decode), it
+ * uses a fixed 128 MiB array of this library in device memory instead (one
+ * per GPU the library runs on, held until the process ends); a request
+ * whose attn_fwd_workspace_bytes exceeds 128 MiB returns ATTN_E_WORKSPACE.
+ * Nothing is allocated or freed: no hipMalloc, hipFree or allocating
+ * library routine.  Its contents on entry are ignored (every byte a call
+ * reads is written by that call first).  All calls on one GPU share that
+ * array: calls that overlap in time on one GPU (on different streams, or
+ * from different threads) race and produce undefined results -- serialize
+ * them.  Errors as attn_fwd.                                               */
+int attn_fwd_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                     const attn_paged_kv* paged, const attn_params* p,
+                     const attn_tensor* out, float* row_stats, void* stream);
 
 /* Packed variable-length batch ("HF Attention Normalizers", "Packed
  * Variable-Length Attention": FlashAttention-style packed Q/K/V with

@@ -33,13 +33,13 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["attn_fwd", "attn_fwd_varlen", "attn_fwd_workspace_bytes", "attn_strerror",
                             "attn_last_error_detail", "attn_abi_version", "attn_bwd",
                             "attn_bwd_workspace_bytes", "attn_fwd_path", "attn_fwd_varlen_path",
-                            "attn_bwd_path"])
+                            "attn_bwd_path", "attn_fwd_noalloc"])
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 6
+    assert apn.attn_abi_version() == 7
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -344,3 +344,19 @@ def test_bwd_path(lib):
     m = _bm()
     pb.block_mask = ctypes.pointer(m)
     assert path_of(_t(Q), _t(KV), pb)[0] == 2
+
+
+def test_noalloc_rejects_oversized_workspace(lib):
+    # the sparse decode lists of 64 sequences x 32 heads over 64 splits of
+    # 512 keys need far more than the fixed 128 MiB scratch: rejected before
+    # anything runs (no device is touched)
+    q = _t((64, 32, 1, 128))
+    cache = _t((70000, 16, 8, 128))
+    r = lib.attn_fwd_noalloc(ctypes.byref(q), ctypes.byref(cache), ctypes.byref(cache),
+                             ctypes.byref(_paged(max_blocks=2048)), ctypes.byref(_p(norm=2)),
+                             ctypes.byref(q), None, None)
+    assert r == 3 and "scratch" in apn.attn_last_error_detail()
+    r = lib.attn_fwd_noalloc(ctypes.byref(q), ctypes.byref(cache), ctypes.byref(cache),
+                             ctypes.byref(_paged(max_blocks=2048)), ctypes.byref(_p(norm=9)),
+                             ctypes.byref(q), None, None)
+    assert r == 1
