@@ -197,6 +197,21 @@ def _check(status):
         raise AttnError(status, attn_last_error_detail())
 
 
+def _on_stream(stream, device, *tensors):
+    """The raw stream handle to enqueue on (torch's current stream when
+    ``stream`` is None).  Tensors allocated here for the call (outputs,
+    workspace) are marked as used by a foreign stream, so torch's caching
+    allocator does not hand their memory to other work before the kernels
+    on that stream have finished."""
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    ext = torch.cuda.ExternalStream(stream, device=device)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(ext)
+    return stream
+
+
 def attn_fwd_workspace_bytes(q, k, v, *, normalizer, causal=False, window=0, softcap=0.0,
                              scaling=None, paged=None):
     """Workspace bytes ``attn_fwd`` needs for these arguments."""
@@ -244,23 +259,25 @@ def attn_fwd(q, k, v, out=None, row_stats=None, *, normalizer, causal=False, win
     [B, 1 or Hq, q-blocks, max_kv_blocks] with ascending block indices).
     """
     lib = load_library()
+    new_out = None
     if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        out = new_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
                                   or tuple(row_stats.shape) != (*q.shape[:3], 2)):
         raise ValueError("row_stats must be a contiguous float32 tensor [B, Hq, Lq, 2]")
     pd = _paged_desc(paged)
     p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
                 block_mask)
+    new_ws = None
     if workspace is None:
         nbytes = attn_fwd_workspace_bytes(q, k, v, normalizer=normalizer, causal=causal,
                                           window=window, softcap=softcap, scaling=scaling,
                                           paged=paged)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        workspace = new_ws = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+                              if nbytes else None)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream = _on_stream(stream, q.device, new_out, new_ws)
     st = lib.attn_fwd(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)), ctypes.byref(_desc(v)),
                       ctypes.byref(pd) if pd is not None else None, ctypes.byref(p),
                       ctypes.byref(_desc(out)),
@@ -283,8 +300,7 @@ def attn_fwd_noalloc(q, k, v, out, row_stats=None, *, normalizer, causal=False, 
     pd = _paged_desc(paged)
     p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
                 block_mask)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream = _on_stream(stream, q.device)
     _check(lib.attn_fwd_noalloc(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)),
                                 ctypes.byref(_desc(v)),
                                 ctypes.byref(pd) if pd is not None else None, ctypes.byref(p),
@@ -313,8 +329,9 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
             raise ValueError(f"{name} must be a contiguous int32 tensor [num_seqs + 1]")
     if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries")
+    new_out = None
     if out is None:
-        out = torch.empty(query.shape, dtype=query.dtype, device=query.device)
+        out = new_out = torch.empty(query.shape, dtype=query.dtype, device=query.device)
     if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
                                   or tuple(row_stats.shape) != (query.shape[1], query.shape[0], 2)):
         raise ValueError("row_stats must be a contiguous float32 tensor [Hq, total_q, 2]")
@@ -325,8 +342,7 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
     vl.num_seqs = cu_seqlens_q.numel() - 1
     vl.max_seqlen_q = int(max_seqlen_q)
     p = _params(normalizer, causal, window, softcap, scaling, query.shape[-1], sinks, query.shape[1])
-    if stream is None:
-        stream = torch.cuda.current_stream(query.device).cuda_stream
+    stream = _on_stream(stream, query.device, new_out)
     st = lib.attn_fwd_varlen(ctypes.byref(_desc(view(query))), ctypes.byref(_desc(view(key))),
                              ctypes.byref(_desc(view(value))), ctypes.byref(vl), ctypes.byref(p),
                              ctypes.byref(_desc(view(out))),
@@ -365,18 +381,23 @@ def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, so
     if (row_stats is None or row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
             or tuple(row_stats.shape) != (*q.shape[:3], 2)):
         raise ValueError("row_stats must be the forward's float32 [B, Hq, Lq, 2]")
-    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
-    ds = torch.empty(q.shape[1], dtype=torch.float32, device=q.device) if sink_grad else None
+    fresh = []
+
+    def alloc(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=q.device)
+        fresh.append(t)
+        return t
+    dq = alloc(q.shape, q.dtype) if dq is None else dq
+    dk = alloc(k.shape, k.dtype) if dk is None else dk
+    dv = alloc(v.shape, v.dtype) if dv is None else dv
+    ds = alloc(q.shape[1], torch.float32) if sink_grad else None
     p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
     qd, kd, vd = _desc(q), _desc(k), _desc(v)
     n = ctypes.c_size_t(0)
     _check(lib.attn_bwd_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
                                         ctypes.byref(p), ctypes.byref(n)))
-    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws = alloc(max(n.value, 1), torch.uint8)
+    stream = _on_stream(stream, q.device, *fresh)
     od = ctypes.byref(_desc(out)) if out is not None else None
     _check(lib.attn_bwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), od,
                         ctypes.byref(_desc(dout)), row_stats.data_ptr(), ctypes.byref(p),

@@ -112,6 +112,17 @@ def traffic_for(kernel_key):
     return int(k["read_bytes"] + k["write_bytes"])
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), else the platform's."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine() or "host"
+
+
 def cpu_baseline(cfg, budget_s=15.0):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -139,7 +150,8 @@ def cpu_baseline(cfg, budget_s=15.0):
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows_done} query rows x {len(cfg.normalizers)} normalizers of {cfg.name} "
-                      f"(fp64 NumPy oracle, one row per call), {dt:.1f} s on {platform.processor() or 'host'}"}
+                      f"(fp64 NumPy oracle, one row per call), {dt:.1f} s",
+            "cpu": cpu_model(), "logical_cpus": os.cpu_count()}
 
 
 def extra_prefill(apn, W, dev, reps=10):

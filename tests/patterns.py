@@ -34,14 +34,37 @@ def workers():
 
 
 _POOL = None
+_ONE_THREAD = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def _worker_init():
+    # one BLAS thread per worker: the workers already use every core
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
 
 
 def pool():
-    """One pool of spawned worker processes for the whole test session."""
+    """One pool of spawned worker processes for the whole test session, each
+    limited to one BLAS thread (spawned children read these variables at
+    start-up; the parent's own settings are restored)."""
     global _POOL
     if _POOL is None:
-        _POOL = concurrent.futures.ProcessPoolExecutor(
-            max_workers=workers(), mp_context=multiprocessing.get_context("spawn"))
+        saved = {k: os.environ.get(k) for k in _ONE_THREAD}
+        os.environ.update({k: "1" for k in _ONE_THREAD})
+        try:
+            _POOL = concurrent.futures.ProcessPoolExecutor(
+                max_workers=workers(), mp_context=multiprocessing.get_context("spawn"),
+                initializer=_worker_init)
+            _POOL.submit(int).result()  # start the workers while the variables hold
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
     return _POOL
 
 

@@ -104,3 +104,27 @@ def test_deterministic_repeat():
         a = gpu_fwd(q, k, k, norm, True, 0, 0.0, 0.125)
         b = gpu_fwd(q, k, k, norm, True, 0, 0.0, 0.125)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("norm", NORMS)
+def test_foreign_stream(norm):
+    # a caller-supplied stream: outputs and the decode workspace the binding
+    # allocates are tied to that stream; results equal the default stream's
+    cfg = W.PagedDecode("dec_stream", 3, 8, 2, 128, "bf16", 16, 200, 1500, 0.09, seed=81)
+    x = W.make_paged(cfg, device="cuda")
+    paged = {"block_table": x.block_table, "seq_lens": x.seq_lens,
+             "block_size": x.block_size, "max_blocks": x.max_blocks}
+    ref, _ = apn.attn_fwd(x.q, x.k_cache, x.v_cache, normalizer=norm, causal=True,
+                          scaling=cfg.scaling, paged=paged)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        o, _ = apn.attn_fwd(x.q, x.k_cache, x.v_cache, normalizer=norm, causal=True,
+                            scaling=cfg.scaling, paged=paged, stream=s.cuda_stream)
+        outs.append(o)
+        torch.empty(1 << 20, device="cuda").fill_(float("nan"))  # churn the caching allocator
+    s.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)

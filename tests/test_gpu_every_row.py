@@ -22,6 +22,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _prefill_every_row(cfg, norm, bh_list):
+    import time
+    t0 = time.time()
     q, k, v = W.make_prefill(cfg)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.empty_like(qd)
@@ -44,13 +46,16 @@ def _prefill_every_row(cfg, norm, bh_list):
     else:
         for x in bh_list:
             pats[x] = gpu_pattern_prefill(kd, run, bh=x)
+    t1 = time.time()
     del qd, kd, vd, out
     torch.cuda.empty_cache()
     jobs = slice_jobs(q.float().numpy(), k.float().numpy(), v.float().numpy(), out_g, st_g, pats,
                       norm, cfg.causal, cfg.window, cfg.softcap, cfg.scaling, "bf16", bh_list,
                       cfg.Hq // cfg.Hkv, chunk=2048 if len(bh_list) > 16 else 512,
                       where=cfg.name)
+    t2 = time.time()
     worst, nrows, fails = run_jobs(jobs)
+    print(f"timing: gpu+inputs {t1 - t0:.1f} s, jobs {t2 - t1:.1f} s, oracle {time.time() - t2:.1f} s")
     assert nrows == len(bh_list) * cfg.Lq
     assert not fails, "\n".join(fails[:20])
     print(f"{cfg.name} {norm}: {nrows} rows, out max-abs {worst:.3e}")
