@@ -38,7 +38,7 @@ from .normalizers import (
 )
 from .attention import (attention_forward, paged_attention_forward, gather_paged_kv,
                         varlen_attention_forward)
-from .backward import attention_backward
+from .backward import attention_backward, varlen_attention_backward
 
 __all__ = [
     "allowed_mask",
@@ -54,4 +54,5 @@ __all__ = [
     "gather_paged_kv",
     "varlen_attention_forward",
     "attention_backward",
+    "varlen_attention_backward",
 ]

@@ -98,3 +98,37 @@ def attention_backward(q, k, v, dout, normalizer, causal=False, window=0, softca
                 dk[b, kv, idx] += np.outer(draw, q[b, h, i])
                 dv[b, kv, idx] += np.outer(p, dout[b, h, i])
     return dq, dk, dv, dsinks
+
+
+def varlen_attention_backward(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, normalizer,
+                              causal=False, window=0, softcap=0.0, scaling=None, sinks=None):
+    """Gradients of ``varlen_attention_forward`` ("HF Attention Normalizers",
+    "Packed Variable-Length Attention": the packed path has a full backward).
+
+    q, dout [total_q, Hq, D]; k, v [total_k, Hkv, D]; request r owns query
+    tokens cu_seqlens_q[r]..cu_seqlens_q[r+1] and key tokens
+    cu_seqlens_k[r]..cu_seqlens_k[r+1] and is differentiated as a batch entry
+    of its own (``attention_backward`` on its slices).  Returns dq [total_q,
+    Hq, D], dk, dv [total_k, Hkv, D] (tokens outside every request: 0) and,
+    for softmax1 with ``sinks``, dsinks [Hq] summed over the requests."""
+    q, k, v, dout = (_as_f64(x) for x in (q, k, v, dout))
+    cq = [int(x) for x in np.asarray(cu_seqlens_q)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k)]
+    Hq = q.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dsinks = np.zeros(Hq) if (normalizer == "softmax1" and sinks is not None) else None
+    tr = lambda x: np.transpose(x, (1, 0, 2))[None]
+    for r in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[r], cq[r + 1], ck[r], ck[r + 1]
+        if q1 == q0:
+            continue
+        g = attention_backward(tr(q[q0:q1]), tr(k[k0:k1]), tr(v[k0:k1]), tr(dout[q0:q1]),
+                               normalizer, causal, window, softcap, scaling, sinks=sinks)
+        dq[q0:q1] += np.transpose(g[0][0], (1, 0, 2))
+        dk[k0:k1] += np.transpose(g[1][0], (1, 0, 2))
+        dv[k0:k1] += np.transpose(g[2][0], (1, 0, 2))
+        if dsinks is not None:
+            dsinks += g[3]
+    return dq, dk, dv, dsinks
