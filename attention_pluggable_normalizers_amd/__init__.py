@@ -16,6 +16,7 @@ from .binding import (
     attn_abi_version,
     attn_bwd,
     attn_bwd_path,
+    attn_bwd_varlen,
     attn_fwd,
     attn_fwd_noalloc,
     attn_fwd_path,
@@ -39,6 +40,7 @@ __all__ = [
     "attn_abi_version",
     "attn_bwd",
     "attn_bwd_path",
+    "attn_bwd_varlen",
     "attn_fwd",
     "attn_fwd_noalloc",
     "attn_fwd_path",

@@ -90,6 +90,11 @@ def load_library(path=None):
                              ctypes.c_void_p, P(_Params), P(_Tensor), P(_Tensor), P(_Tensor),
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_varlen.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor),
+                                    ctypes.c_void_p, P(_Varlen), P(_Params), P(_Tensor),
+                                    P(_Tensor), P(_Tensor), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_bwd_varlen.restype = ctypes.c_int
     lib.attn_bwd_workspace_bytes.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Params),
                                              P(ctypes.c_size_t)]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_int
@@ -309,6 +314,27 @@ def attn_fwd_noalloc(q, k, v, out, row_stats=None, *, normalizer, causal=False, 
     return out, row_stats
 
 
+def _packed_view(t):
+    """[tokens, heads, D] -> the [1, heads, tokens, D] view (no copy)."""
+    return t.permute(1, 0, 2).unsqueeze(0)
+
+
+def _varlen_desc(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q):
+    if query.dim() != 3 or key.dim() != 3 or value.dim() != 3:
+        raise ValueError("packed query/key/value are [tokens, heads, head_dim]")
+    for t, name in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor [num_seqs + 1]")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries")
+    vl = _Varlen()
+    vl.cu_seqlens_q = cu_seqlens_q.data_ptr()
+    vl.cu_seqlens_k = cu_seqlens_k.data_ptr()
+    vl.num_seqs = cu_seqlens_q.numel() - 1
+    vl.max_seqlen_q = int(max_seqlen_q)
+    return vl
+
+
 def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None,
                     row_stats=None, *, normalizer, causal=False, window=0, softcap=0.0,
                     scaling=None, stream=None, sinks=None):
@@ -322,25 +348,14 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
     results; returns ``(out, row_stats)``.
     """
     lib = load_library()
-    if query.dim() != 3 or key.dim() != 3 or value.dim() != 3:
-        raise ValueError("packed query/key/value are [tokens, heads, head_dim]")
-    for t, name in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
-        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 tensor [num_seqs + 1]")
-    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries")
+    vl = _varlen_desc(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)
     new_out = None
     if out is None:
         out = new_out = torch.empty(query.shape, dtype=query.dtype, device=query.device)
     if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
                                   or tuple(row_stats.shape) != (query.shape[1], query.shape[0], 2)):
         raise ValueError("row_stats must be a contiguous float32 tensor [Hq, total_q, 2]")
-    view = lambda t: t.permute(1, 0, 2).unsqueeze(0)  # [1, heads, tokens, D], no copy
-    vl = _Varlen()
-    vl.cu_seqlens_q = cu_seqlens_q.data_ptr()
-    vl.cu_seqlens_k = cu_seqlens_k.data_ptr()
-    vl.num_seqs = cu_seqlens_q.numel() - 1
-    vl.max_seqlen_q = int(max_seqlen_q)
+    view = _packed_view
     p = _params(normalizer, causal, window, softcap, scaling, query.shape[-1], sinks, query.shape[1])
     stream = _on_stream(stream, query.device, new_out)
     st = lib.attn_fwd_varlen(ctypes.byref(_desc(view(query))), ctypes.byref(_desc(view(key))),
@@ -353,11 +368,13 @@ def attn_fwd_varlen(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
 
 
 def attn_bwd_path(q, k, v, dout, *, normalizer, causal=False, window=0, softcap=0.0,
-                  scaling=None, sinks=None, dq=None, dk=None, dv=None, out=None):
+                  scaling=None, sinks=None, dq=None, dk=None, dv=None, out=None,
+                  block_mask=None):
     """Name of the kernel family ``attn_bwd`` takes ("bwd_mfma", "bwd_per_row"
     or "none"); gradients default to tensors laid out like q, k, v."""
     lib = load_library()
-    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
+                block_mask)
     path = ctypes.c_int(-1)
     od = ctypes.byref(_desc(out)) if out is not None else None
     _check(lib.attn_bwd_path(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)),
@@ -370,13 +387,14 @@ def attn_bwd_path(q, k, v, dout, *, normalizer, causal=False, window=0, softcap=
 
 def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, softcap=0.0,
              scaling=None, sinks=None, dq=None, dk=None, dv=None, sink_grad=False, out=None,
-             stream=None):
+             stream=None, block_mask=None):
     """Gradients of ``attn_fwd`` for the same q, k, v and parameters, given the
     forward's ``row_stats`` and the upstream gradient ``dout``: returns
     ``(dq, dk, dv, dsinks)`` (``dsinks`` float32 [Hq] when ``sink_grad``,
     softmax1 only, else None).  ``out`` (optional): the forward's output; the
     softmax family then takes its row constant from dout . out (one pass
-    fewer)."""
+    fewer).  ``block_mask``: the forward's (kv_num_blocks, kv_indices,
+    block_q, block_k)."""
     lib = load_library()
     if (row_stats is None or row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
             or tuple(row_stats.shape) != (*q.shape[:3], 2)):
@@ -391,7 +409,8 @@ def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, so
     dk = alloc(k.shape, k.dtype) if dk is None else dk
     dv = alloc(v.shape, v.dtype) if dv is None else dv
     ds = alloc(q.shape[1], torch.float32) if sink_grad else None
-    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1])
+    p = _params(normalizer, causal, window, softcap, scaling, q.shape[-1], sinks, q.shape[1],
+                block_mask)
     qd, kd, vd = _desc(q), _desc(k), _desc(v)
     n = ctypes.c_size_t(0)
     _check(lib.attn_bwd_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
@@ -404,6 +423,49 @@ def attn_bwd(q, k, v, dout, row_stats, *, normalizer, causal=False, window=0, so
                         ctypes.byref(_desc(dq)), ctypes.byref(_desc(dk)), ctypes.byref(_desc(dv)),
                         ds.data_ptr() if ds is not None else None, ws.data_ptr(), n.value,
                         stream))
+    return dq, dk, dv, ds
+
+
+def attn_bwd_varlen(query, key, value, dout, row_stats, cu_seqlens_q, cu_seqlens_k,
+                    max_seqlen_q, *, normalizer, causal=False, window=0, softcap=0.0,
+                    scaling=None, sinks=None, dq=None, dk=None, dv=None, sink_grad=False,
+                    out=None, stream=None):
+    """Gradients of ``attn_fwd_varlen`` ("HF Attention Normalizers", "Packed
+    Variable-Length Attention"): query, dout [total_q, Hq, D], key, value
+    [total_k, Hkv, D], row_stats the forward's float32 [Hq, total_q, 2].
+    Returns ``(dq, dk, dv, dsinks)`` in the packed layouts; tokens outside
+    every request get zeros."""
+    lib = load_library()
+    vl = _varlen_desc(query, key, value, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)
+    if (row_stats is None or row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+            or tuple(row_stats.shape) != (query.shape[1], query.shape[0], 2)):
+        raise ValueError("row_stats must be the forward's float32 [Hq, total_q, 2]")
+    fresh = []
+
+    def alloc(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=query.device)
+        fresh.append(t)
+        return t
+    dq = alloc(query.shape, query.dtype) if dq is None else dq
+    dk = alloc(key.shape, key.dtype) if dk is None else dk
+    dv = alloc(value.shape, value.dtype) if dv is None else dv
+    ds = alloc(query.shape[1], torch.float32) if sink_grad else None
+    p = _params(normalizer, causal, window, softcap, scaling, query.shape[-1], sinks,
+                query.shape[1])
+    view = _packed_view
+    qd, kd, vd = _desc(view(query)), _desc(view(key)), _desc(view(value))
+    n = ctypes.c_size_t(0)
+    _check(lib.attn_bwd_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                                        ctypes.byref(p), ctypes.byref(n)))
+    ws = alloc(max(n.value, 1), torch.uint8)
+    stream = _on_stream(stream, query.device, *fresh)
+    od = ctypes.byref(_desc(view(out))) if out is not None else None
+    _check(lib.attn_bwd_varlen(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), od,
+                               ctypes.byref(_desc(view(dout))), row_stats.data_ptr(),
+                               ctypes.byref(vl), ctypes.byref(p), ctypes.byref(_desc(view(dq))),
+                               ctypes.byref(_desc(view(dk))), ctypes.byref(_desc(view(dv))),
+                               ds.data_ptr() if ds is not None else None, ws.data_ptr(), n.value,
+                               stream))
     return dq, dk, dv, ds
 
 

@@ -18,7 +18,11 @@
 //     rows i of the head's G query heads that see j: dV_j = sum p_ij dO_i,
 //     dK_j = sum draw_ij q_i (c_i from the query kernel)
 //   sink kernel (softmax1 with sinks): d b_h = -sum_i p_sink,i c_i.
-// Contiguous K/V only; every sum runs in a fixed order (deterministic).
+// Contiguous K/V, padded or packed ("HF Attention Normalizers", "Packed
+// Variable-Length Attention": each request differentiated as a batch entry
+// of its own, tokens outside every request get zero gradients), with or
+// without a block mask (keys outside the listed blocks carry no weight and
+// no gradient).  Every sum runs in a fixed order (deterministic).
 
 #include <string.h>
 
@@ -30,6 +34,20 @@ namespace attn {
 namespace {
 
 constexpr int kMaxD = 256;
+constexpr int kMaxBlocks = 16384;  // block masks: query / key blocks per bitmap in LDS
+
+// Packed batch: the request that holds token `tok` under the cumulative
+// offsets cu[0..nreq] is the last r < nreq with cu[r] <= tok (the caller
+// checks that tok lies inside it).
+__device__ __forceinline__ int request_of(const int32_t* cu, int nreq, int tok) {
+  int lo = 0, hi = nreq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= tok) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
 
 // Weight of one score from the row statistics, and u = sqrt(p) for entmax.
 template <int NORM>
@@ -66,28 +84,80 @@ template <typename T, int NORM>
 __global__ __launch_bounds__(64) void bwd_query_kernel(BwdArgs w) {
   const FwdArgs& a = w.f;
   __shared__ float qs[kMaxD], dos[kMaxD], dsv[64];
-  const int64_t row = blockIdx.x;  // ((b * Hq) + h) * Lq + i
+  __shared__ unsigned kb_bits[kMaxBlocks / 32];  // block mask: listed key blocks of this row
+  const int64_t row = blockIdx.x;  // ((b * Hq) + h) * Lq + i; packed: h * Lq + token
   const int lane = threadIdx.x, D = a.D;
-  const int i = (int)(row % a.Lq);
-  const int64_t bh = row / a.Lq;
-  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq), kvh = h / a.G;
-  const T* qrow = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)i * a.q_sl;
-  const T* dorow = (const T*)w.dout + (int64_t)b * w.do_sb + (int64_t)h * w.do_sh + (int64_t)i * w.do_sl;
+  int b = 0, h, i, tok, nq, live, key0 = 0;
+  bool inside = true;
+  if (!a.cu_q) {
+    i = (int)(row % a.Lq);
+    const int64_t bh = row / a.Lq;
+    h = (int)(bh % a.Hq);
+    b = (int)(bh / a.Hq);
+    tok = i;
+    nq = a.Lq;
+    live = a.Lk;
+  } else {
+    tok = (int)(row % a.Lq);
+    h = (int)(row / a.Lq);
+    i = nq = live = 0;
+    inside = a.B > 0;
+    if (inside) {
+      b = request_of(a.cu_q, a.B, tok);
+      int q0, q1, k0, k1;
+      varlen_ranges(a, b, q0, q1, k0, k1);
+      inside = tok >= q0 && tok < q1;
+      i = tok - q0;
+      nq = q1 - q0;
+      live = k1 - k0;
+      key0 = k0;
+    }
+  }
+  const int kvh = h / a.G;
+  const int64_t ba = a.cu_q ? 0 : b;  // batch index of the arrays
+  T* dqrow = (T*)w.dq + ba * w.dq_sb + (int64_t)h * w.dq_sh + (int64_t)tok * w.dq_sl;
+  if (!inside) {  // token outside every request: zero gradient, no sink term
+    for (int d = lane; d < D; d += 64) dqrow[d] = from_f32<T>(0.f);
+    if (lane == 0) {
+      w.crow[row] = 0.f;
+      if (NORM == ATTN_SOFTMAX1 && w.dsinks) w.srow[row] = 0.f;
+    }
+    return;
+  }
+  const T* qrow = (const T*)a.q + ba * a.q_sb + (int64_t)h * a.q_sh + (int64_t)tok * a.q_sl;
+  const T* dorow = (const T*)w.dout + ba * w.do_sb + (int64_t)h * w.do_sh + (int64_t)tok * w.do_sl;
   for (int d = lane; d < D; d += 64) {
     qs[d] = to_f32(qrow[d]);
     dos[d] = to_f32(dorow[d]);
   }
-  __syncthreads();
-  const T* kb = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-  const T* vb = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+  const T* kb = (const T*)a.k + ba * a.k_sb + (int64_t)kvh * a.k_sh + (int64_t)key0 * a.k_sl;
+  const T* vb = (const T*)a.v + ba * a.v_sb + (int64_t)kvh * a.v_sh + (int64_t)key0 * a.v_sl;
   int lo, hi;
-  key_range(i, a.Lq, a.Lk, a.causal, a.window, lo, hi);
+  key_range(i, nq, live, a.causal, a.window, lo, hi);
   const float st0 = a.stats[row * 2], st1 = a.stats[row * 2 + 1];
-  T* dqrow = (T*)w.dq + (int64_t)b * w.dq_sb + (int64_t)h * w.dq_sh + (int64_t)i * w.dq_sl;
+
+  // block mask: a bitmap of the key blocks listed for this row's query block
+  const bool bm = a.bm_num != nullptr;
+  if (bm) {
+    const int nkb = (live + a.bm_bk - 1) / a.bm_bk;
+    for (int x = lane; x < (nkb + 31) / 32; x += 64) kb_bits[x] = 0u;
+    __syncthreads();
+    int n;
+    const int32_t* list = a.bm_idx + bm_list(a, b, h, i / a.bm_bq, n);
+    for (int e = lane; e < n; e += 64)
+      if (bm_entry_ok(list, e, nkb)) atomicOr(&kb_bits[list[e] >> 5], 1u << (list[e] & 31));
+  }
+  __syncthreads();
+  auto allowed = [&](int j) -> bool {
+    if (!bm) return true;
+    const int c = j / a.bm_bk;
+    return (kb_bits[c >> 5] >> (c & 31)) & 1u;
+  };
 
   // pass 1: the row constant of the Jacobian
   float c1 = 0.f, c2 = 0.f;
   for (int j = lo + lane; j < hi; j += 64) {
+    if (!allowed(j)) continue;
     float dsdraw, u;
     const float s = score(a, dot_row(qs, kb + (int64_t)j * a.k_sl, D), dsdraw);
     const float p = weight<NORM>(s, st0, st1, u);
@@ -119,7 +189,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(BwdArgs w) {
   for (int base = lo; base < hi; base += 64) {
     const int j = base + lane;
     float draw = 0.f;
-    if (j < hi) {
+    if (j < hi && allowed(j)) {
       float dsdraw, u;
       const float s = score(a, dot_row(qs, kb + (int64_t)j * a.k_sl, D), dsdraw);
       const float p = weight<NORM>(s, st0, st1, u);
@@ -166,32 +236,85 @@ template <typename T, int NORM>
 __global__ __launch_bounds__(64) void bwd_key_kernel(BwdArgs w) {
   const FwdArgs& a = w.f;
   __shared__ float ks[kMaxD], vs[kMaxD], pv[64], gv[64];
-  const int64_t krow = blockIdx.x;  // ((b * Hkv) + kvh) * Lk + j
+  __shared__ unsigned qb_bits[kMaxBlocks / 32];  // block mask: query blocks that list this key's block
+  const int64_t krow = blockIdx.x;  // ((b * Hkv) + kvh) * Lk + j; packed: kvh * Lk + token
   const int lane = threadIdx.x, D = a.D;
-  const int j = (int)(krow % a.Lk);
-  const int64_t bk = krow / a.Lk;
-  const int kvh = (int)(bk % a.Hkv), b = (int)(bk / a.Hkv);
-  const T* kp = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh + (int64_t)j * a.k_sl;
-  const T* vp = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh + (int64_t)j * a.v_sl;
+  int b = 0, kvh, j, tok, nq, live, qtok0 = 0;
+  bool inside = true;
+  if (!a.cu_q) {
+    j = (int)(krow % a.Lk);
+    const int64_t bk = krow / a.Lk;
+    kvh = (int)(bk % a.Hkv);
+    b = (int)(bk / a.Hkv);
+    tok = j;
+    nq = a.Lq;
+    live = a.Lk;
+  } else {
+    tok = (int)(krow % a.Lk);
+    kvh = (int)(krow / a.Lk);
+    j = nq = live = 0;
+    inside = a.B > 0;
+    if (inside) {
+      b = request_of(a.cu_k, a.B, tok);
+      int q0, q1, k0, k1;
+      varlen_ranges(a, b, q0, q1, k0, k1);
+      inside = tok >= k0 && tok < k1;
+      j = tok - k0;
+      nq = q1 - q0;
+      live = k1 - k0;
+      qtok0 = q0;
+    }
+  }
+  const int64_t ba = a.cu_q ? 0 : b;  // batch index of the arrays
+  T* dkr = (T*)w.dk + ba * w.dk_sb + (int64_t)kvh * w.dk_sh + (int64_t)tok * w.dk_sl;
+  T* dvr = (T*)w.dv + ba * w.dv_sb + (int64_t)kvh * w.dv_sh + (int64_t)tok * w.dv_sl;
+  if (!inside) {  // token outside every request: zero gradients
+    for (int d = lane; d < D; d += 64) {
+      dkr[d] = from_f32<T>(0.f);
+      dvr[d] = from_f32<T>(0.f);
+    }
+    return;
+  }
+  const T* kp = (const T*)a.k + ba * a.k_sb + (int64_t)kvh * a.k_sh + (int64_t)tok * a.k_sl;
+  const T* vp = (const T*)a.v + ba * a.v_sb + (int64_t)kvh * a.v_sh + (int64_t)tok * a.v_sl;
   for (int d = lane; d < D; d += 64) {
     ks[d] = to_f32(kp[d]);
     vs[d] = to_f32(vp[d]);
   }
   __syncthreads();
   int ilo, ihi;
-  query_range(j, a.Lq, a.Lk, a.causal, a.window, ilo, ihi);
+  query_range(j, nq, live, a.causal, a.window, ilo, ihi);
+  const bool bm = a.bm_num != nullptr;
   float ak[kMaxD / 64], av[kMaxD / 64];
 #pragma unroll
   for (int t = 0; t < kMaxD / 64; ++t) ak[t] = av[t] = 0.f;
   for (int hh = 0; hh < a.G; ++hh) {
     const int h = kvh * a.G + hh;
-    const T* qb = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
-    const T* dob = (const T*)w.dout + (int64_t)b * w.do_sb + (int64_t)h * w.do_sh;
-    const int64_t row0 = ((int64_t)b * a.Hq + h) * a.Lq;
+    const T* qb = (const T*)a.q + ba * a.q_sb + (int64_t)h * a.q_sh + (int64_t)qtok0 * a.q_sl;
+    const T* dob = (const T*)w.dout + ba * w.do_sb + (int64_t)h * w.do_sh + (int64_t)qtok0 * w.do_sl;
+    const int64_t row0 = (ba * a.Hq + h) * a.Lq + qtok0;
+    // block mask: bit r set when query block r of head h lists key j's block
+    // (rebuilt per head unless the mask is shared by all heads)
+    if (bm && ihi > ilo && (hh == 0 || a.bm_heads != 1)) {
+      const int kbj = j / a.bm_bk, nkb = (live + a.bm_bk - 1) / a.bm_bk;
+      const int r0 = ilo / a.bm_bq, r1 = (ihi - 1) / a.bm_bq + 1;
+      __syncthreads();  // the previous head's readers are done
+      for (int x = (r0 >> 5) + lane; x < (r1 + 31) >> 5; x += 64) qb_bits[x] = 0u;
+      __syncthreads();
+      for (int r = r0 + lane; r < r1; r += 64) {
+        int n;
+        const int32_t* list = a.bm_idx + bm_list(a, b, h, r, n);
+        bool hit = false;
+        for (int e = 0; e < n; ++e) hit |= list[e] == kbj && bm_entry_ok(list, e, nkb);
+        if (hit) atomicOr(&qb_bits[r >> 5], 1u << (r & 31));
+      }
+      __syncthreads();
+    }
     for (int base = ilo; base < ihi; base += 64) {
       const int i = base + lane;
       float p = 0.f, g = 0.f;
-      if (i < ihi) {
+      const bool on = i < ihi && (!bm || ((qb_bits[(i / a.bm_bq) >> 5] >> ((i / a.bm_bq) & 31)) & 1u));
+      if (on) {
         const float st0 = a.stats[(row0 + i) * 2], st1 = a.stats[(row0 + i) * 2 + 1];
         float raw = 0.f, dP = 0.f;
         const T* qr = qb + (int64_t)i * a.q_sl;
@@ -232,8 +355,6 @@ __global__ __launch_bounds__(64) void bwd_key_kernel(BwdArgs w) {
       __syncthreads();
     }
   }
-  T* dkr = (T*)w.dk + (int64_t)b * w.dk_sb + (int64_t)kvh * w.dk_sh + (int64_t)j * w.dk_sl;
-  T* dvr = (T*)w.dv + (int64_t)b * w.dv_sb + (int64_t)kvh * w.dv_sh + (int64_t)j * w.dv_sl;
 #pragma unroll
   for (int t = 0; t < kMaxD / 64; ++t) {
     const int d = lane + 64 * t;
@@ -249,7 +370,8 @@ __global__ __launch_bounds__(64) void bwd_sink_kernel(BwdArgs w) {
   const FwdArgs& a = w.f;
   const int h = blockIdx.x, lane = threadIdx.x;
   float s = 0.f;
-  for (int b = 0; b < a.B; ++b) {
+  const int nb = a.cu_q ? 1 : a.B;  // packed: one row array over all requests
+  for (int b = 0; b < nb; ++b) {
     const int64_t row0 = ((int64_t)b * a.Hq + h) * a.Lq;
     for (int i = lane; i < a.Lq; i += 64) s += w.srow[row0 + i];
   }
@@ -265,7 +387,8 @@ hipError_t launch_bwd_sinks(const BwdArgs& w, hipStream_t stream) {
 template <typename T, int NORM>
 hipError_t launch_norm(const BwdArgs& w, hipStream_t stream) {
   const FwdArgs& a = w.f;
-  const int64_t qrows = (int64_t)a.B * a.Hq * a.Lq, krows = (int64_t)a.B * a.Hkv * a.Lk;
+  const int64_t nb = a.cu_q ? 1 : a.B;  // packed: [1, H, tokens] arrays
+  const int64_t qrows = nb * a.Hq * a.Lq, krows = nb * a.Hkv * a.Lk;
   if (qrows) bwd_query_kernel<T, NORM><<<dim3((unsigned)qrows), dim3(64), 0, stream>>>(w);
   if (krows) bwd_key_kernel<T, NORM><<<dim3((unsigned)krows), dim3(64), 0, stream>>>(w);
   if (NORM == ATTN_SOFTMAX1 && w.dsinks && a.Hq)
@@ -309,7 +432,10 @@ static int bwd_prepare(const attn_tensor* q, const attn_tensor* k, const attn_te
   memset(w, 0, sizeof(*w));
   int st = validate_fwd_args(q, k, v, p, &w->f, need_data);
   if (st) return st;
-  if (w->f.bm_num) return bwd_fail(ATTN_E_UNSUPPORTED, "the backward takes no block mask");
+  // block masks: the key kernel keeps a bitmap of query blocks in LDS (the
+  // forward's validation bounds the key blocks the same way)
+  if (w->f.bm_num && (w->f.Lq + w->f.bm_bq - 1) / w->f.bm_bq > kMaxBlocks)
+    return bwd_fail(ATTN_E_UNSUPPORTED, "block mask has more than 16384 query blocks");
   if (!dout || !dq || !dk || !dv) return bwd_fail(ATTN_E_INVALID, "dout, dq, dk or dv descriptor is NULL");
   if (!same_shape(dout, q) || !same_shape(dq, q))
     return bwd_fail(ATTN_E_INVALID, "dout and dq must match q in shape and dtype");
@@ -394,6 +520,46 @@ extern "C" int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_t
     w.srow = w.crow + (size_t)w.f.B * w.f.Hq * w.f.Lq;
     e = w.f.dtype == ATTN_BF16 ? launch_t<bf16_t>(w, s) : launch_t<float>(w, s);
   }
+  if (e != hipSuccess) return bwd_fail(ATTN_E_LAUNCH, "HIP launch failed");
+  return ATTN_OK;
+}
+
+extern "C" int attn_bwd_varlen(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                               const attn_tensor* out, const attn_tensor* dout,
+                               const float* row_stats, const attn_varlen* varlen,
+                               const attn_params* p, const attn_tensor* dq, const attn_tensor* dk,
+                               const attn_tensor* dv, float* dsinks, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  BwdArgs w;
+  int st = bwd_prepare(q, k, v, out, dout, row_stats, p, dq, dk, dv, &w, true);
+  if (st) return st;
+  if (!varlen) return bwd_fail(ATTN_E_INVALID, "varlen descriptor is NULL");
+  if (w.f.bm_num) return bwd_fail(ATTN_E_UNSUPPORTED, "block masks apply to a padded batch only");
+  if (q->shape[0] != 1 || k->shape[0] != 1)
+    return bwd_fail(ATTN_E_INVALID, "packed q, k, v must have batch extent 1");
+  if (varlen->num_seqs < 0 || varlen->max_seqlen_q < 0)
+    return bwd_fail(ATTN_E_INVALID, "num_seqs and max_seqlen_q must be >= 0");
+  if (varlen->num_seqs > 0 && (!varlen->cu_seqlens_q || !varlen->cu_seqlens_k))
+    return bwd_fail(ATTN_E_INVALID, "cu_seqlens_q or cu_seqlens_k is NULL");
+  if (dsinks && w.f.norm != ATTN_SOFTMAX1)
+    return bwd_fail(ATTN_E_INVALID, "sink gradients apply to softmax1 only");
+  const size_t need = (size_t)w.f.Hq * w.f.Lq * 2 * sizeof(float);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return bwd_fail(ATTN_E_WORKSPACE, "workspace smaller than 8 bytes per query head and token");
+  // The kernels tell a packed batch by a non-NULL cu_q; with no requests the
+  // arrays are never read (every token lies outside and gets zeros), so any
+  // non-NULL address stands in.
+  static const int32_t no_requests[2] = {0, 0};
+  w.f.cu_q = varlen->num_seqs > 0 ? varlen->cu_seqlens_q : no_requests;
+  w.f.cu_k = varlen->num_seqs > 0 ? varlen->cu_seqlens_k : no_requests;
+  w.f.B = varlen->num_seqs;
+  w.f.max_q = varlen->max_seqlen_q;
+  w.dsinks = dsinks;
+  w.crow = (float*)workspace;
+  w.srow = w.crow + (size_t)w.f.Hq * w.f.Lq;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const hipError_t e = w.f.dtype == ATTN_BF16 ? launch_t<bf16_t>(w, s) : launch_t<float>(w, s);
   if (e != hipSuccess) return bwd_fail(ATTN_E_LAUNCH, "HIP launch failed");
   return ATTN_OK;
 }

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 /* Status codes. */
 typedef enum attn_status {
@@ -290,9 +290,12 @@ int attn_fwd_workspace_bytes(const attn_tensor* q, const attn_tensor* k,
  *       dimension contiguous, 16-byte aligned).  softmax / softmax1 then take
  *       the row constant of the Jacobian, sum_j p dP = dout . out, from it
  *       and skip one pass over the keys; the sparse normalizers ignore it.
- * Contiguous K/V, no block mask.  bf16 inputs with D = 64, 128 or 256 (16-byte
- * aligned, strides multiples of 8 elements) run on the matrix cores (bf16
- * operands, fp32 accumulation); everything else on per-row fp32 kernels.
+ * Contiguous K/V.  p->block_mask as in the forward: keys outside the listed
+ * blocks carry no weight and receive no gradient (at most 16384 query
+ * blocks and 16384 key blocks; the per-row kernels).  bf16 inputs with
+ * D = 64, 128 or 256 (16-byte aligned, strides multiples of 8 elements) and
+ * no block mask run on the matrix cores (bf16 operands, fp32
+ * accumulation); everything else on per-row fp32 kernels.
  * Every output is written in full.  workspace: attn_bwd_workspace_bytes
  * (the larger of 8 bytes per query row, and 384 bytes per 32 query rows of
  * each (batch, head) plus 4 bytes per query row, rounded up to 256 bytes,
@@ -304,6 +307,25 @@ int attn_bwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
              const attn_params* p,
              const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
              float* dsinks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_bwd_varlen -- attn_bwd over a packed variable-length batch ("HF
+ * Attention Normalizers", "Packed Variable-Length Attention": the packed
+ * path carries a full backward).  Layouts as attn_fwd_varlen: q, out,
+ * dout, dq [1, Hq, total_q, D]; k, v, dk, dv [1, Hkv, total_k, D];
+ * row_stats [1, Hq, total_q, 2] from the attn_fwd_varlen call with the same
+ * q, k, v, varlen and parameters.  Each request is differentiated as a
+ * batch entry of its own; dk / dv sum over the request's query heads of
+ * each key/value head only.  Tokens outside every request get zero
+ * gradients (every output is written in full); dsinks sums over all
+ * requests.  max_seqlen_q is not used.  No block mask.  Runs on the per-row
+ * fp32 kernels.  workspace: 8 bytes per (query head, packed query token)
+ * (attn_bwd_workspace_bytes of the packed descriptors is enough).  Errors
+ * as attn_bwd.                                                            */
+int attn_bwd_varlen(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                    const attn_tensor* out, const attn_tensor* dout, const float* row_stats,
+                    const attn_varlen* varlen, const attn_params* p,
+                    const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
+                    float* dsinks, void* workspace, size_t workspace_bytes, void* stream);
 
 /* attn_bwd_path -- the attn_path (ATTN_PATH_BWD_MFMA or ATTN_PATH_BWD_PER_ROW,
  * ATTN_PATH_NONE when there is nothing to compute) that attn_bwd would take

@@ -33,13 +33,13 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["attn_fwd", "attn_fwd_varlen", "attn_fwd_workspace_bytes", "attn_strerror",
                             "attn_last_error_detail", "attn_abi_version", "attn_bwd",
                             "attn_bwd_workspace_bytes", "attn_fwd_path", "attn_fwd_varlen_path",
-                            "attn_bwd_path", "attn_fwd_noalloc"])
+                            "attn_bwd_path", "attn_fwd_noalloc", "attn_bwd_varlen"])
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert apn.attn_abi_version() == 7
+    assert apn.attn_abi_version() == 8
     for code in range(5):
         assert apn.attn_strerror(code).startswith("ATTN_")
     assert "unknown" in apn.attn_strerror(77)
@@ -260,10 +260,67 @@ def test_backward_validation(lib):
     r, d = call(out=_t((2, 8, 64, 32)))
     assert r == 1 and "out" in d
     pb = _p()
+    m = _bm(bq=1, bk=1)  # 64 query blocks: accepted; see test_bwd_path
+    pb.block_mask = ctypes.pointer(m)
+    r, d = call(p=pb, wsn=8)
+    assert r == 3 and "workspace" in d
+
+
+def test_bwd_block_mask_query_block_limit(lib):
+    # the per-row key kernel keeps a bitmap of at most 16384 query blocks
+    q, kv = _t((1, 2, 16385, 64)), _t((1, 2, 64, 64))
+    pb = _p()
+    m = _bm(bq=1, bk=64)
+    pb.block_mask = ctypes.pointer(m)
+    path = ctypes.c_int(-1)
+    r = lib.attn_bwd_path(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv), None,
+                          ctypes.byref(q), ctypes.byref(pb), ctypes.byref(q), ctypes.byref(kv),
+                          ctypes.byref(kv), ctypes.byref(path))
+    assert r == 2 and "16384 query blocks" in apn.attn_last_error_detail()
+    m.block_q = 2
+    r = lib.attn_bwd_path(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv), None,
+                          ctypes.byref(q), ctypes.byref(pb), ctypes.byref(q), ctypes.byref(kv),
+                          ctypes.byref(kv), ctypes.byref(path))
+    assert r == 0 and B.PATH_NAMES[path.value] == "bwd_per_row"
+
+
+def _vl(num_seqs=3, max_q=50, cu_q=0x5000, cu_k=0x6000):
+    vl = B._Varlen()
+    vl.cu_seqlens_q, vl.cu_seqlens_k, vl.num_seqs, vl.max_seqlen_q = cu_q, cu_k, num_seqs, max_q
+    return vl
+
+
+def test_bwd_varlen_validation(lib):
+    # every case fails validation before anything is launched
+    def call(q=None, kv=None, vl="default", p=None, stats=0x9000, wsn=1 << 20, dsinks=None):
+        q = q or _t((1, 8, 100, 64))
+        kv = kv or _t((1, 2, 120, 64))
+        vl = _vl() if vl == "default" else vl
+        r = lib.attn_bwd_varlen(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv), None,
+                                ctypes.byref(q), stats,
+                                ctypes.byref(vl) if vl is not None else None,
+                                ctypes.byref(p or _p()), ctypes.byref(q), ctypes.byref(kv),
+                                ctypes.byref(kv), dsinks, 0x9100, wsn, None)
+        return r, apn.attn_last_error_detail()
+    r, d = call(vl=None)
+    assert r == 1 and "varlen" in d
+    r, d = call(vl=_vl(num_seqs=-1))
+    assert r == 1 and "num_seqs" in d
+    r, d = call(vl=_vl(cu_q=0))
+    assert r == 1 and "cu_seqlens" in d
+    r, d = call(q=_t((2, 8, 100, 64)), kv=_t((2, 2, 120, 64)))
+    assert r == 1 and "batch extent" in d
+    r, d = call(stats=None)
+    assert r == 1 and "row_stats" in d
+    r, d = call(dsinks=0x9200)
+    assert r == 1 and "softmax1" in d
+    r, d = call(wsn=8 * 8 * 100 - 1)
+    assert r == 3 and "workspace" in d
+    pb = _p()
     m = _bm()
     pb.block_mask = ctypes.pointer(m)
     r, d = call(p=pb)
-    assert r == 2 and "block mask" in d
+    assert r == 2 and "padded batch" in d
 
 
 def _fwd_path(lib, q, k, v, p, out=None, paged=None):
@@ -343,7 +400,7 @@ def test_bwd_path(lib):
     pb = _p()
     m = _bm()
     pb.block_mask = ctypes.pointer(m)
-    assert path_of(_t(Q), _t(KV), pb)[0] == 2
+    assert path_of(_t(Q), _t(KV), pb) == (0, "bwd_per_row")
 
 
 def test_noalloc_rejects_oversized_workspace(lib):
