@@ -1321,15 +1321,21 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       first_x = false;
       buf = (float*)((char*)(lds + SC::NX * KT) + wave * SC::WREG_X) + lane;
       keyed = false;
-      cap = SC::SCAP_X;
+      cap = SC::SCAP_X - 1;  // the last entry takes values that are not kept
       cnt = 0;
     }
-    double c = 0.0, s1 = 0.0, s2 = 0.0;      // above the floor
-    double ch = 0.0, s1h = 0.0, s2h = 0.0;   // above hi
+    // Totals above the floor and above hi, and the window values (floor, hi]
+    // into the lane's buffer, without branches per value: every value takes
+    // the same instructions (masked operands; a window value that is not
+    // kept is written to the buffer's last entry, which holds no candidate
+    // here).
+    double s1 = 0.0, s2 = 0.0, s1h = 0.0, s2h = 0.0;  // sums of y = z - mref
     float mn = INFINITY, mnh = INFINITY;
+    int na = 0, nh = 0;  // counts above the floor, above hi
     const double mref = (double)mrun;
     if (pending) cnt = 0;  // solved rows keep their support
     int fits = pending ? 1 : 0;
+    constexpr int kSpare = SC::SCAP_X - 1;  // entry that takes the values not kept
     k_prologue(sx);
     cur = 0;
     for (int u = 0; u < ts.n; ++u) {
@@ -1342,51 +1348,35 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
         f32x16 s[C::NKB];
         qk_tile<C>(kl, qreg, l32, g, s);
         const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
-        float vv[C::NKB][16];  // stored-domain values
-        if (pending) {
+        const bool collect = __any(fits != 0);  // some row still keeps its window
 #pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
+        for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float v = CAP ? zval<true>(s[kb][r], cz, sc_over_cap, capz) : s[kb][r];
-              if (edge) {
-                const int key = s_key(k0, kb, r, g);
-                if (key < mine.lo || key >= mine.hi) v = -INFINITY;
-              }
-              vv[kb][r] = v;
-              const float z = stored_z<CAP>(v, cz);
-              if ((double)z > floor_) {
-                const double y = (double)z - mref;
-                c += 1.0;
-                s1 += y;
-                s2 += y * y;
-                mn = fminf(mn, z);
-                if (v > hi_v) {
-                  ch += 1.0;
-                  s1h += y;
-                  s2h += y * y;
-                  mnh = fminf(mnh, z);
-                }
-              }
+          for (int r = 0; r < 16; ++r) {
+            float v = CAP ? zval<true>(s[kb][r], cz, sc_over_cap, capz) : s[kb][r];
+            if (edge) {
+              const int key = s_key(k0, kb, r, g);
+              if (key < mine.lo || key >= mine.hi) v = -INFINITY;
             }
-          }
-        }
-        if (__any(pending && fits)) {
-          if (pending && fits) {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                if (vv[kb][r] > floor_v && !(vv[kb][r] > hi_v)) {
-                  if (cnt < cap) {
-                    buf[cnt * 64] = vv[kb][r];
-                    if (SC::KEYS && keyed) kbuf[cnt * 64] = (u16)s_key(k0, kb, r, g);
-                    ++cnt;
-                  } else {
-                    fits = 0;
-                  }
-                }
-              }
+            const float z = stored_z<CAP>(v, cz);
+            const bool above = pending && v > floor_v;  // z > floor_
+            const bool top = above && v > hi_v;
+            const double y = (double)z - mref;
+            const double ya = above ? y : 0.0, yh = top ? y : 0.0;
+            na += above ? 1 : 0;
+            s1 += ya;
+            s2 += ya * ya;
+            mn = fminf(mn, above ? z : INFINITY);
+            nh += top ? 1 : 0;
+            s1h += yh;
+            s2h += yh * yh;
+            mnh = fminf(mnh, top ? z : INFINITY);
+            if (collect) {
+              const bool want = above && !top && fits != 0;
+              const bool keep = want && cnt < cap;
+              fits = want && !keep ? 0 : fits;
+              buf[(keep ? cnt : kSpare) * 64] = v;
+              cnt += keep ? 1 : 0;
             }
           }
         }
@@ -1394,6 +1384,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       k_done(sx, cur);
     }
     wait_vmcnt<0>();
+    double c = (double)na, ch = (double)nh;
     c += partner_d(c);
     s1 += partner_d(s1);
     s2 += partner_d(s2);

@@ -213,8 +213,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 }
 
 // 16 bytes per lane from buffer offset voff + soff to LDS byte lds_addr + 16 l.
+// The compiler's hazard check does not look inside inline assembly, so the
+// block starts with the wait states its operands may need: the transfer
+// takes its LDS address from M0, which needs one after a scalar write of M0
+// (the compiler often writes M0 right before the block; its own LDS
+// transfers get an s_nop there), and a scalar operand written by a vector
+// instruction (an SGPR restored from a spill lane) needs five before a
+// vector-memory read.  Without them the transfer can land at the previous
+// transfer's address.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
 
