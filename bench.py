@@ -41,6 +41,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources of the prefill kernels (the counter summary is tied to their hash)
 PREFILL_SRCS = [os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", f)
                 for f in ("prefill.hip", "tiles.h", "common.h")]
+DECODE_SRCS = [os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", f)
+               for f in ("decode.hip", "common.h")]
 
 
 def credited_pairs(cfg):
@@ -98,15 +100,17 @@ def time_launches(f, reps, warmup):
     return median_us(evs)
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the prefill source changed since the counters were taken."""
+def traffic_for(kernel_key, family="prefill"):
+    """HBM bytes per launch (all kernels of the call) from the committed
+    counter summary, or None when the family's kernel sources changed since
+    the counters were taken."""
+    srcs = PREFILL_SRCS if family == "prefill" else DECODE_SRCS
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in PREFILL_SRCS)).hexdigest()
+        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("prefill_src_sha256") != src or kernel_key not in rec.get("kernels", {}):
+    if rec.get(f"{family}_src_sha256") != src or kernel_key not in rec.get("kernels", {}):
         return None
     k = rec["kernels"][kernel_key]
     return int(k["read_bytes"] + k["write_bytes"])
@@ -181,6 +185,23 @@ def extra_prefill(apn, W, dev, reps=10):
     return res
 
 
+def largest_roofline(W, workloads):
+    """Roofline of the slowest kernel of the largest workload (the
+    Qwen3-1.7B-shaped sweep: 2 x 16 heads x 8192 x 8192 keys, every score
+    scale), from the launch times measured in extra_prefill."""
+    best = None
+    for cfg in (W.qwen(0.5), W.qwen(1.0), W.qwen(2.0)):
+        rec = workloads[cfg.name]
+        for n, r in rec["per_normalizer"].items():
+            if best is None or r["us"] > best[2]:
+                best = (cfg, n, r["us"], rec["credited_flop_per_launch"])
+    cfg, n, us, flops = best
+    achieved = flops / (us * 1e-6) / 1e12
+    return {"kernel": f"prefill {n} ({cfg.name})", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(f"{cfg.name}:{n}")}
+
+
 def backward_bench(apn, cfg, q, k, v, norms, pairs, reps=20):
     """Backward (attn_bwd) of the same workload from the forward's row
     statistics and output: median time and TFLOP/s on the conventional
@@ -230,7 +251,8 @@ def decode_bench(apn, W, dev, reps, chunk=0):
            "per_normalizer": dres,
            "roofline": {"kernel": f"paged decode {dom}", "bound": "hbm",
                         "achieved": dres[dom]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": dres[dom]["frac_hbm_peak"]}}
+                        "frac": dres[dom]["frac_hbm_peak"],
+                        "traffic": traffic_for(f"{dcfg.name}:{dom}", "decode")}}
     if chunk:
         res["chunked_prefill"] = chunk_bench(apn, x, dcfg, lens, paged, dev, chunk)
     return res
@@ -427,6 +449,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         result["prefill_workloads"] = extra_prefill(apn, W, dev)
+        result["roofline_largest"] = largest_roofline(W, result["prefill_workloads"])
     if not args.no_decode:
         result["decode"] = decode_bench(apn, W, dev, max(3, args.steps),
                                         chunk=0 if args.no_extra else 512)
