@@ -3,7 +3,11 @@
 // The K/V cache is read page by page through the block table ("HF Attention
 // Normalizers", "Differentiable Paged Attention": physical pages are read
 // directly, no gathered K/V copy).  The keys of a sequence are cut into
-// splits of kSplit keys; one wave handles one (split, kv head, sequence) and
+// splits (kSplit keys for the sparse normalizers; for the softmax family a
+// size chosen per launch so that the last round of workgroups is nearly
+// full); a one-wave plan kernel lists the live splits of all sequences in
+// order, and the split kernel's grid walks that list, so no empty split sits
+// among the live ones.  One wave handles one (split, kv head, sequence) and
 // serves all G = Hq / Hkv query heads of the group, so every K/V byte is read
 // once:
 //
@@ -21,6 +25,10 @@
 //           g(z - tau) V over the support only, so V rows of zero-weight keys
 //           are never read.
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "common.h"
 
 namespace attn {
@@ -31,8 +39,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSplit = 512;      // keys per split
+constexpr int kSplit = 512;      // keys per split (sparse normalizers)
 static_assert((kSplit & (kSplit - 1)) == 0, "split lists store key offsets masked to the split");
+// Softmax family: the split size is chosen per launch among the multiples of
+// 32 in [kMinSplit, kMaxSplit] (see decode_plan_kernel); the sparse
+// normalizers keep kSplit.  The workspace starts with a header of ints --
+// [0] the split size, [1] the number of live splits, [2 + b] the first live
+// split of sequence b in the packed list (B + 1 entries) -- rounded up to 64
+// words; the partials or split lists follow.  At most 61 16-key blocks per
+// split, so a lane per block fits the wave.
+constexpr int kMinSplit = 448;
+constexpr int kMaxSplit = 960;
+__host__ __device__ inline int64_t hdr_words(int B) { return ((int64_t)B + 3 + 63) / 64 * 64; }
 constexpr int kSolveCap = 2048;  // candidate capacity of the sparse solver (LDS)
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -65,7 +83,30 @@ __device__ __forceinline__ int64_t key_row(const int32_t* table, int bs, int nb,
 // Partial record per (sequence, query head, split): m, l, 2 pad, acc[D] (fp32;
 // acc 16-byte aligned).
 __device__ __forceinline__ float* partial_ptr(float* ws, const FwdArgs& a, int b, int qh, int s, int ns) {
-  return ws + (((int64_t)b * a.Hq + qh) * ns + s) * (a.D + 4);
+  return ws + hdr_words(a.B) + (((int64_t)b * a.Hq + qh) * ns + s) * (a.D + 4);
+}
+
+// Split of a softmax-family workgroup: the plan's packed list of live splits
+// (sequence-major) is walked by `item`; items past its end get b = -1.
+struct SplitRef {
+  int b, s, ks;
+};
+__device__ __forceinline__ SplitRef split_of(const FwdArgs& a, const float* ws, int item) {
+  const int* hdr = (const int*)ws;
+  SplitRef r;
+  r.ks = __builtin_amdgcn_readfirstlane(hdr[0]);
+  r.b = -1;
+  r.s = 0;
+  if (item >= __builtin_amdgcn_readfirstlane(hdr[1])) return r;
+  int lo = 0, hi = a.B;  // last b with first[b] <= item
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(hdr[2 + mid]) <= item) lo = mid;
+    else hi = mid;
+  }
+  r.b = lo;
+  r.s = seq_view(a, lo).lo / r.ks + (item - __builtin_amdgcn_readfirstlane(hdr[2 + lo]));
+  return r;
 }
 
 // Threshold search step over the candidate set L = {z > t} (see the
@@ -118,6 +159,7 @@ struct SparseLists {
 };
 __device__ __forceinline__ SparseLists sparse_lists(float* ws, const FwdArgs& a, int ns) {
   const int64_t rn = (int64_t)a.B * a.Hq * ns;
+  ws += hdr_words(a.B);  // after the plan's header
   SparseLists l;
   l.smax = ws;
   l.sfloor = ws + rn;
@@ -257,14 +299,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
   __shared__ float ps[32][17];    // weights of the 32 keys of a chunk, per head (padded)
 
   const int lane = threadIdx.x;
-  const int s = blockIdx.x % ns;
-  const int bh = blockIdx.x / ns;
-  const int kvh = bh % a.Hkv;
-  const int b = bh / a.Hkv;
+  // the plan's packed live splits, kv head fastest; the grid's tail past
+  // them exits
+  const int kvh = blockIdx.x % a.Hkv;
+  const SplitRef r = split_of(a, ws, blockIdx.x / a.Hkv);
+  if (r.b < 0) return;
+  const int b = r.b, s = r.s, ksp = r.ks;
   const int G = a.G;
   const SeqView sv = seq_view(a, b);
-  const int k_begin = max(sv.lo, s * kSplit);
-  const int k_end = min(sv.n, (s + 1) * kSplit);
+  const int k_begin = max(sv.lo, s * ksp);
+  const int k_end = min(sv.n, (s + 1) * ksp);
 
   const int hh = lane & 15;        // query head of this lane's MFMA column
   const bool head_ok = hh < G;
@@ -273,16 +317,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
   const bf16_t* kc = (const bf16_t*)a.k + (int64_t)kvh * a.k_sh;
   const bf16_t* vc = (const bf16_t*)a.v + (int64_t)kvh * a.v_sh;
 
-  if (k_begin >= k_end) {
-    // empty split: neutral partial (m = -inf, l = 0, acc = 0)
-    if (NORM == ATTN_SOFTMAX || NORM == ATTN_SOFTMAX1) {
-      for (int h = 0; h < G; ++h) {
-        float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
-        for (int d = lane; d < D + 4; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
-      }
-    }
-    return;
-  }
+  if (k_begin >= k_end) return;  // (a live split is never empty; kept as a guard)
 
   // Q^T operand: lane l holds head l%16, dims 32c + 8 (l/16) .. +7
   bf16x8 qreg[NKC];
@@ -495,31 +530,24 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
   const int wpg = blockDim.x >> 6;
   const int ngrp = a.Hkv / wpg;
   const int kvh = (blockIdx.x % ngrp) * wpg + wave;
-  const int bs_ = blockIdx.x / ngrp;
-  const int s = bs_ % ns;
-  const int b = bs_ / ns;
+  // the plan's packed live splits; the grid's tail past them exits
+  const SplitRef r = split_of(a, ws, blockIdx.x / ngrp);
+  if (r.b < 0) return;
+  const int b = r.b, s = r.s, ksp = r.ks;
   float (*ps)[GM] = (float (*)[GM])(dyn_lds + wave * 32 * GM);
   const int G = a.G;
   const SeqView sv = seq_view(a, b);
-  const int k_begin = max(sv.lo, s * kSplit);
-  const int k_end = min(sv.n, (s + 1) * kSplit);
+  const int k_begin = max(sv.lo, s * ksp);
+  const int k_end = min(sv.n, (s + 1) * ksp);
 
   const int hh = lane & 15;
   const bool head_ok = hh < G;
   const int qh = kvh * G + (head_ok ? hh : 0);
 
-  if (k_begin >= k_end) {
-    if (!SPARSE) {
-      for (int h = 0; h < G; ++h) {
-        float* pp = partial_ptr(ws, a, b, kvh * G + h, s, ns);
-        for (int d = lane; d < D + 4; d += 64) pp[d] = d == 0 ? -INFINITY : 0.f;
-      }
-    }
-    return;
-  }
+  if (k_begin >= k_end) return;  // (a live split is never empty; kept as a guard)
 
-  // blocks of the split: lane i < nblk holds block i's K and V row
-  // addresses and live byte ranges; other lanes hold empty ranges
+  // blocks of the split: lane i < nblk (at most 61) holds block i's K and V
+  // row addresses and live byte ranges; other lanes hold empty ranges
   const int kb = k_begin & ~15;
   const int nblk = (k_end - kb + 15) >> 4;
   const int nchunk = (nblk + 1) >> 1;
@@ -755,10 +783,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
   const int tid = threadIdx.x;
   __shared__ float red[256];
   __shared__ f32x4 part[NG][CH];
-  const float* rec = ws + (int64_t)row * ns * REC;
+  // the row's live splits s0 .. s0 + nsp - 1 (the plan's list)
+  const int* hdr = (const int*)ws;
+  const int nsp = hdr[2 + b + 1] - hdr[2 + b];
+  const int s0 = seq_view(a, b).lo / hdr[0];
+  const float* rec = ws + hdr_words(a.B) + ((int64_t)row * ns + s0) * REC;
   // global max over the splits (softmax1 also counts its logit-0 sink)
   float m = -INFINITY;
-  for (int s = tid; s < ns; s += 256) m = fmaxf(m, rec[(int64_t)s * REC]);
+  for (int s = tid; s < nsp; s += 256) m = fmaxf(m, rec[(int64_t)s * REC]);
   red[tid] = m;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -772,7 +804,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
   if (NORM == ATTN_SOFTMAX1) M = fmaxf(M, sink2);
   const float mref = M == -INFINITY ? 0.f : M;
   float l = 0.f;
-  for (int s = tid; s < ns; s += 256) {
+  for (int s = tid; s < nsp; s += 256) {
     const float* pp = rec + (int64_t)s * REC;
     l += pp[1] * __builtin_amdgcn_exp2f(pp[0] - mref);
   }
@@ -788,7 +820,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(FwdArgs a, const fl
   // weighted sum of the acc chunks
   const int g = tid / CH, c = tid - g * CH;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = g; s < ns; s += NG) {
+  for (int s = g; s < nsp; s += NG) {
     const float* pp = rec + (int64_t)s * REC;
     const float w = __builtin_amdgcn_exp2f(pp[0] - mref);
     const f32x4 v = *(const f32x4*)(pp + 4 + 4 * c);
@@ -1129,6 +1161,62 @@ __global__ __launch_bounds__(256) void decode_sparse_solve_kernel(FwdArgs a, flo
   }
 }
 
+// Split size of a softmax-family launch.  The split workgroups all do the
+// same work (a full split) except at sequence ends, so the launch ends when
+// the last of ceil(items / slots) rounds of workgroups does; with `slots`
+// workgroups resident on the GPU, a size whose item count leaves the last
+// round nearly empty wastes most of a round.  Among the multiples of 32 in
+// [kMinSplit, kMaxSplit] the size with the fullest last round (items / slots
+// over its ceiling) is taken, the larger one on ties (the sparse
+// normalizers pass their fixed kSplit); one wave, lane i summing sequences
+// i, i + 64, ...  Writes the header: the size, and the packed list of live
+// splits that the split kernels walk in grid order, so no workgroup of the
+// grid's head is an empty split.
+__global__ __launch_bounds__(64) void decode_plan_kernel(FwdArgs a, float* ws, int slots, int groups,
+                                                          int fixed_ks) {
+  const int lane = threadIdx.x;
+  float best = -1.f;
+  int best_ks = fixed_ks > 0 ? fixed_ks : kSplit;
+  for (int ks = kMinSplit; fixed_ks == 0 && ks <= kMaxSplit; ks += 32) {
+    int items = 0;
+    for (int b = lane; b < a.B; b += 64) {
+      const SeqView sv = seq_view(a, b);
+      if (sv.n > sv.lo) items += (sv.n + ks - 1) / ks - sv.lo / ks;
+    }
+    items = wave_sum(items) * groups;
+    const float rounds = (float)items / (float)slots;
+    const float eff = rounds <= 0.f ? 0.f : rounds / ceilf(rounds);
+    if (eff >= best) {
+      best = eff;
+      best_ks = ks;
+    }
+  }
+  // packed list: first live split of each sequence (exclusive prefix sum)
+  int* hdr = (int*)ws;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    int n = 0;
+    if (b < a.B) {
+      const SeqView sv = seq_view(a, b);
+      if (sv.n > sv.lo) n = (sv.n + best_ks - 1) / best_ks - sv.lo / best_ks;
+    }
+    int incl = n;  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (b < a.B) hdr[2 + b] = base + incl - n;
+    base += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) {
+    hdr[0] = best_ks;
+    hdr[1] = base;
+    hdr[2 + a.B] = base;
+  }
+}
+
 // Page size a multiple of 16 and cache rows that fit the 32-bit buffer
 // offsets of the paged16 split kernel.
 bool paged16(const FwdArgs& a) {
@@ -1139,7 +1227,27 @@ bool paged16(const FwdArgs& a) {
 
 int num_splits(const FwdArgs& a) {
   const int64_t maxlen = (int64_t)a.max_blocks * a.block_size;
-  return (int)((maxlen + kSplit - 1) / kSplit);
+  const int ks = (a.norm == ATTN_SOFTMAX || a.norm == ATTN_SOFTMAX1) ? kMinSplit : kSplit;
+  return (int)((maxlen + ks - 1) / ks);
+}
+
+// Workgroups of `kern` resident on the current device at once (cached per
+// device and kernel configuration).
+int resident_groups(const void* kern, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const auto key = std::make_tuple(dev, kern, threads, lds);
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, lds) != hipSuccess || per <= 0)
+    per = 1;
+  return cache[key] = cus * per;
 }
 
 template <int D, int NORM>
@@ -1164,6 +1272,8 @@ hipError_t launch_d(const FwdArgs& a, void* workspace, hipStream_t stream) {
     auto go = [&](auto kern) {
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
+      const int slots = resident_groups((const void*)kern, 64 * wpg, lds);
+      decode_plan_kernel<<<dim3(1), dim3(64), 0, stream>>>(a, ws, slots, a.Hkv / wpg, sparse ? kSplit : 0);
       kern<<<g16, b16, lds, stream>>>(a, ws, ns);
       return hipSuccess;
     };
@@ -1172,15 +1282,25 @@ hipError_t launch_d(const FwdArgs& a, void* workspace, hipStream_t stream) {
     else if (gm == 8) e0 = cap ? go(decode_split_paged16_kernel<D, NORM, true, 8>) : go(decode_split_paged16_kernel<D, NORM, false, 8>);
     else e0 = cap ? go(decode_split_paged16_kernel<D, NORM, true, 16>) : go(decode_split_paged16_kernel<D, NORM, false, 16>);
     if (e0 != hipSuccess) return e0;
-  } else if (a.G <= 4) {
-    if (cap) decode_split_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
-    else decode_split_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
-  } else if (a.G <= 8) {
-    if (cap) decode_split_kernel<D, NORM, true, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
-    else decode_split_kernel<D, NORM, false, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
   } else {
-    if (cap) decode_split_kernel<D, NORM, true, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
-    else decode_split_kernel<D, NORM, false, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+    {
+      const bool sparse = NORM == ATTN_SPARSEMAX || NORM == ATTN_ENTMAX15;
+      const void* k1 = a.G <= 4 ? (const void*)decode_split_kernel<D, NORM, false, 4>
+                                : a.G <= 8 ? (const void*)decode_split_kernel<D, NORM, false, 8>
+                                           : (const void*)decode_split_kernel<D, NORM, false, 16>;
+      decode_plan_kernel<<<dim3(1), dim3(64), 0, stream>>>(a, ws, resident_groups(k1, 64, 0), a.Hkv,
+                                                           sparse ? kSplit : 0);
+    }
+    if (a.G <= 4) {
+      if (cap) decode_split_kernel<D, NORM, true, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
+      else decode_split_kernel<D, NORM, false, 4><<<g1, b1, 0, stream>>>(a, ws, ns);
+    } else if (a.G <= 8) {
+      if (cap) decode_split_kernel<D, NORM, true, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
+      else decode_split_kernel<D, NORM, false, 8><<<g1, b1, 0, stream>>>(a, ws, ns);
+    } else {
+      if (cap) decode_split_kernel<D, NORM, true, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+      else decode_split_kernel<D, NORM, false, 16><<<g1, b1, 0, stream>>>(a, ws, ns);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1220,9 +1340,12 @@ bool decode_supported(const FwdArgs& a) {
 
 size_t decode_workspace_bytes(const FwdArgs& a) {
   if (a.norm == ATTN_SOFTMAX || a.norm == ATTN_SOFTMAX1)
-    return (size_t)a.B * a.Hq * num_splits(a) * (a.D + 4) * sizeof(float);
-  // split lists: max, floor, length, z and key offset per (row, split)
-  return (size_t)a.B * a.Hq * num_splits(a) * (3 * sizeof(float) + kSplit * (sizeof(float) + sizeof(uint16_t)));
+    return (size_t)hdr_words(a.B) * sizeof(float) +
+           (size_t)a.B * a.Hq * num_splits(a) * (a.D + 4) * sizeof(float);
+  // header, then the split lists: max, floor, length, z and key offset per
+  // (row, split)
+  return (size_t)hdr_words(a.B) * sizeof(float) +
+         (size_t)a.B * a.Hq * num_splits(a) * (3 * sizeof(float) + kSplit * (sizeof(float) + sizeof(uint16_t)));
 }
 
 hipError_t launch_decode(const FwdArgs& a, void* workspace, hipStream_t stream) {

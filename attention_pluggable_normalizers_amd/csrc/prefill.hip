@@ -359,11 +359,14 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
           s[kb][r] = off < span ? s[kb][r] : -INFINITY;
         }
     }
-    float mt = -INFINITY;
+    // row max and (below) row sum in four independent chains: a single chain
+    // of dependent instructions per tile stalls the wave
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+    float mt = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mt = pair_max(mt);
     const float mt2 = CAP ? mt : mt * c2;
     m_true = fmaxf(m_true, mt2);
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
       for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
     }
     const float mref = m_use == -INFINITY ? 0.f : m_use;
-    float ps = 0.f;
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pk[2 * C::NKB];
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
@@ -388,12 +391,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
       for (int r = 0; r < 16; ++r) {
         p[r] = CAP ? __builtin_amdgcn_exp2f(s[kb][r] - mref)
                    : __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -mref));
-        ps += p[r];
+        ps4[r & 3] += p[r];
       }
       pk[2 * kb] = p_operand(p);
       pk[2 * kb + 1] = p_operand(p + 8);
     }
-    lsum += ps;
+    lsum += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -748,7 +751,8 @@ __device__ __forceinline__ void compact_buf(float* buf, u16* kbuf, int& cnt, flo
 // g(z - tau) * v over its half of the head dimension in fp32 (V rows are read
 // through the key indices, and for a paged cache through the block table; no
 // score is recomputed).  The weights sum to one up to rounding; the output
-// is divided by their fp32 sum.
+// is divided by the fp32 sum of the weights as they enter the sums (rounded
+// to bf16 where entries are taken in pairs).
 template <class C, int NORM, bool CAP>
 __device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, int cnt, int g, float tauf,
                                             float cz, const bf16_t* vbase, int64_t v_sl, int64_t v_sb,
@@ -765,47 +769,81 @@ __device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, i
 #pragma unroll
   for (int d = 0; d < DH; ++d) acc[d] = 0.f;
   float wsum = 0.f;
-  for (int e = 0; __any(e < n); e += U) {
-    float p[U];
-    u32x4 w[U][NV];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int i = e + j;
-      const bool ok = i < n;
-      // past the end: weight 0 and key 0 (a row of this sequence whenever
-      // any lane of the wave has entries)
-      const int slot = !ok ? 0 : (i < n0 ? lead + i * 64 : lead + 32 + (i - n0) * 64);
-      const float v = buf[slot];
-      const int key = ok ? (int)kbuf[slot] : 0;
-      float pw;
-      {
+  // weight and V row (this lane's half) of entry i (past the end: weight 0
+  // and key 0, a row of this sequence whenever any lane of the wave has
+  // entries)
+  auto fetch = [&](int i, float& pj, u32x4 (&wj)[NV]) __attribute__((always_inline)) {
+    const bool ok = i < n;
+    const int slot = !ok ? 0 : (i < n0 ? lead + i * 64 : lead + 32 + (i - n0) * 64);
+    const float v = buf[slot];
+    const int key = ok ? (int)kbuf[slot] : 0;
+    float pw;
+    {
 #pragma clang fp contract(off)
-        const float d = stored_z<CAP>(v, cz) - tauf;
-        pw = d > 0.f ? d : 0.f;
-        if (NORM == ATTN_ENTMAX15) pw = pw * pw;
-      }
-      p[j] = ok ? pw : 0.f;
-      int64_t off;
-      if (pg.row) {
-        const int64_t page = page_of(pg.row, min(key / pg.bs, pg.max_blocks - 1), pg.nblk);
-        off = page * v_sb + (int64_t)(key % pg.bs) * v_sl;
-      } else {
-        off = (int64_t)key * v_sl;
-      }
-      const u32x4* vr = (const u32x4*)(vcol + off);
-#pragma unroll
-      for (int c = 0; c < NV; ++c) w[j][c] = vr[c];
+      const float d = stored_z<CAP>(v, cz) - tauf;
+      pw = d > 0.f ? d : 0.f;
+      if (NORM == ATTN_ENTMAX15) pw = pw * pw;
     }
+    pj = ok ? pw : 0.f;
+    int64_t off;
+    if (pg.row) {
+      const int64_t page = page_of(pg.row, min(key / pg.bs, pg.max_blocks - 1), pg.nblk);
+      off = page * v_sb + (int64_t)(key % pg.bs) * v_sl;
+    } else {
+      off = (int64_t)key * v_sl;
+    }
+    const u32x4* vr = (const u32x4*)(vcol + off);
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      wsum += p[j];
+    for (int c = 0; c < NV; ++c) wj[c] = vr[c];
+  };
+  // entries j, j + 1 taken together: the two weights rounded to bf16 (as the
+  // matrix-core output rounds P; wsum sums the rounded weights) and, per dim,
+  // the two entries' values side by side, so one bf16 dot product adds both
+  // (exact bf16 products, fp32 sums)
+  auto add_pair = [&](float p0, float p1, const u32x4 (&w0)[NV], const u32x4 (&w1)[NV])
+                      __attribute__((always_inline)) {
+    const unsigned pp = pack_bf16(p0, p1);
+    wsum += __uint_as_float(pp << 16) + __uint_as_float(pp & 0xffff0000u);
+    const bf16x2 pb = __builtin_bit_cast(bf16x2, pp);
 #pragma unroll
-      for (int c = 0; c < NV; ++c)
+    for (int c = 0; c < NV; ++c)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[8 * c + 2 * q] += p[j] * __uint_as_float(w[j][c][q] << 16);
-          acc[8 * c + 2 * q + 1] += p[j] * __uint_as_float(w[j][c][q] & 0xffff0000u);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const unsigned a0 = w0[c][q], a1 = w1[c][q];
+        const unsigned lo = (a0 & 0xffffu) | (a1 << 16);      // dim 2q of both
+        const unsigned hi = (a0 >> 16) | (a1 & 0xffff0000u);  // dim 2q + 1 of both
+        acc[8 * c + 2 * q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lo), pb,
+                                                             acc[8 * c + 2 * q], false);
+        acc[8 * c + 2 * q + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), pb,
+                                                                 acc[8 * c + 2 * q + 1], false);
+      }
+  };
+  if constexpr (U % 2 == 0) {
+    for (int e = 0; __any(e < n); e += U) {
+      float p[U];
+      u32x4 w[U][NV];
+#pragma unroll
+      for (int j = 0; j < U; ++j) fetch(e + j, p[j], w[j]);
+#pragma unroll
+      for (int j = 0; j < U; j += 2) add_pair(p[j], p[j + 1], w[j], w[j + 1]);
+    }
+  } else {
+    for (int e = 0; __any(e < n); e += U) {
+      float p[U];
+      u32x4 w[U][NV];
+#pragma unroll
+      for (int j = 0; j < U; ++j) fetch(e + j, p[j], w[j]);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        wsum += p[j];
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[8 * c + 2 * q] += p[j] * __uint_as_float(w[j][c][q] << 16);
+            acc[8 * c + 2 * q + 1] += p[j] * __uint_as_float(w[j][c][q] & 0xffff0000u);
+          }
+      }
     }
   }
   if (row_ok) {
