@@ -270,7 +270,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_
   const int l32 = lane & 31, g = lane >> 5;
   const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   int bh, qb;
-  block_coords_lpt(nqb, bh, qb);
+  block_coords_lpt(nqb, bh, qb, a.paged || a.cu_q, a.Hq, a.Hkv);
   const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
   const int q0 = qb * C::BM;
   const SeqSpan sp = seq_span(a, b, h);
@@ -874,7 +874,7 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   const int l32 = lane & 31, g = lane >> 5;
   const int nqb = (q_extent(a) + C::BM - 1) / C::BM;
   int bh, qb;
-  block_coords_lpt(nqb, bh, qb);
+  block_coords_lpt(nqb, bh, qb, a.paged || a.cu_q, a.Hq, a.Hkv);
   const int b = bh / a.Hq, h = bh - b * a.Hq, kvh = h / a.G;
   const int q0 = qb * C::BM;
   const SeqSpan sp = seq_span(a, b, h);

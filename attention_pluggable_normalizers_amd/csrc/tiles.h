@@ -121,7 +121,14 @@ __device__ __forceinline__ void block_coords(int nqb, int& bh, int& qb) {
 // its range, then the one before, and so on, so its CUs are packed
 // longest-job-first (a per-head order leaves the short blocks of early heads
 // occupying CUs while long blocks of later heads wait).
-__device__ __forceinline__ void block_coords_lpt(int nqb, int& bh, int& qb) {
+//
+// Sequences of different lengths (a paged cache or a packed batch: `spread`)
+// would load the XCDs unevenly with contiguous ranges of whole sequences, so
+// there each XCD takes, from every sequence, the kv heads congruent to it
+// modulo 8 (with their G query heads, which share K/V in its L2): every XCD
+// gets the same share of every sequence.  Needs Hkv a multiple of 8.
+__device__ __forceinline__ void block_coords_lpt(int nqb, int& bh, int& qb, bool spread = false,
+                                                 int Hq = 0, int Hkv = 0) {
   const int nblk = gridDim.x;
   int id = blockIdx.x;
   const bool xcd = (nblk & 7) == 0;
@@ -131,7 +138,15 @@ __device__ __forceinline__ void block_coords_lpt(int nqb, int& bh, int& qb) {
     const int heads = per / nqb;           // whole heads per range
     const int x = id / per, j = id - x * per;
     qb = nqb - 1 - j / heads;
-    bh = x * heads + (j - (j / heads) * heads);
+    const int lh = j - (j / heads) * heads;  // head of the range
+    if (xcd && spread && Hkv % 8 == 0 && Hq % Hkv == 0 && heads % (Hq / 8) == 0) {
+      const int hx = Hq / 8;                 // query heads of one sequence per XCD
+      const int G = Hq / Hkv, b = lh / hx, r = lh - b * hx;
+      const int kk = r / G, g = r - kk * G;  // kv head kk * 8 + x, query head g of it
+      bh = b * Hq + (kk * 8 + x) * G + g;
+    } else {
+      bh = x * heads + lh;
+    }
   } else {
     bh = id / nqb;
     qb = nqb - 1 - (id - bh * nqb);
