@@ -140,6 +140,10 @@ __device__ __forceinline__ void block_coords_lpt(int nqb, int& bh, int& qb, bool
     qb = nqb - 1 - j / heads;
     const int lh = j - (j / heads) * heads;  // head of the range
     if (xcd && spread && Hkv % 8 == 0 && Hq % Hkv == 0 && heads % (Hq / 8) == 0) {
+      // the q-blocks of one head, then the heads of one kv head, run
+      // together: they stream the same K/V tiles through the XCD's L2
+      const int lh = j / nqb;
+      qb = nqb - 1 - (j - lh * nqb);
       const int hx = Hq / 8;                 // query heads of one sequence per XCD
       const int G = Hq / Hkv, b = lh / hx, r = lh - b * hx;
       const int kk = r / G, g = r - kk * G;  // kv head kk * 8 + x, query head g of it
