@@ -542,6 +542,10 @@ struct SparseCfg {
   static constexpr int KEYS_OFF = SCAP_K * 256;            // key indices, from the region start
   static constexpr int WREG_X = (LDS_BYTES - NX * KTILE) / C::NW / 256 * 256;
   static constexpr int SCAP_X = WREG_X / 256 / 8 * 8;      // values per lane, extra passes
+  // histogram pass: 16-bit bin counts, two per word, 32 rows per wave
+  static constexpr int NBIN = WREG_X / 64 < 256 ? WREG_X / 64 / 8 * 8 : 256;
+  static_assert(NBIN >= 64 && NBIN * 64 <= WREG_X, "histogram bins must fit the wave's region");
+  static_assert(KEYS_OFF + SCAP_K * 128 + 4 <= WREG, "keyed layout leaves the region's last word free");
   static_assert(NB * 2 * KTILE <= LDS_BYTES, "output pass stages must fit");
   static_assert(SCAP_K >= 32 && KEYS_OFF + SCAP_K * 128 <= WREG && SCAP_X >= 32 && SCAP_X <= SCAP_F,
                 "candidate buffer too small");
@@ -947,6 +951,8 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   constexpr int kMaxRefloors = 4;
   // longest key range (per workgroup) that takes the lookahead below
   constexpr int kLookaheadKeys = 8192;
+  // crowding below which a row skips the candidate pass (see the lookahead)
+  constexpr float kCrowd = 0.15f;
   int nrefloor = 0;
 
   // The kTop largest lane-block maxima of z this lane has seen, descending.
@@ -976,7 +982,12 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // with S_m the prefix sum; 1.5-entmax: mean - sqrt((1 - ss) / m) with ss the
   // prefix's sum of squared deviations, invalid once ss > 1, which only grows
   // with m).  Both lanes of a row see the same union, so they agree.
-  auto top_floor = [&]() __attribute__((always_inline)) -> double {
+  //
+  // With `crowd`, also the mass the listed values would take above the
+  // smallest of them, sum of g(u_i - u_min) (+inf for a list that is not
+  // full).  A small value means values crowd just below the list's
+  // threshold: the support reaches far beyond the listed values.
+  auto top_floor = [&](float* crowd = nullptr) __attribute__((always_inline)) -> double {
     constexpr int M = 2 * kTop;
     float u[M];
 #pragma unroll
@@ -993,6 +1004,15 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
           u[i] = hi;
           u[i + span] = lo;
         }
+    if (crowd) {
+      float r = 0.f;
+#pragma unroll
+      for (int i = 0; i < M - 1; ++i) {
+        const float d = u[i] - u[M - 1];
+        r += NORM == ATTN_SPARSEMAX ? d : d * d;
+      }
+      *crowd = u[M - 1] > -INFINITY ? r : INFINITY;
+    }
     const double mref = (double)u[0];
     double best = -INFINITY, s1 = 0.0, s2 = 0.0;
 #pragma unroll
@@ -1090,8 +1110,30 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   };
   constexpr Stages<NA> sa{};
   constexpr Stages<SC::NX> sx{};
-  k_prologue(sa);
   int cur = 0;
+  // workgroup OR through one word of K stage 0, called only while no
+  // transfer is in flight (the closing barrier keeps the next transfers from
+  // landing before every wave has read it); the runtime's __syncthreads_or
+  // would take static LDS on top of the dynamic allocation and cost the
+  // second workgroup per CU
+  int* const any_word = (int*)ka_of(0);
+  auto block_any = [&](bool v) __attribute__((always_inline)) {
+    __syncthreads();
+    if (tid == 0) *(volatile int*)any_word = 0;
+    __syncthreads();
+    if (v) *(volatile int*)any_word = 1;
+    __syncthreads();
+    const bool r = *(volatile int*)any_word != 0;
+    __syncthreads();
+    return r;
+  };
+  bool run_a = true;    // workgroup-uniform: some row takes the candidate pass
+  bool voted = false;   // workgroup-uniform: the waves posted crowding counts
+  auto vote_word = [&](int w) __attribute__((always_inline)) {
+    return (volatile int*)((char*)(lds + SC::NA * KT) + w * SC::WREG + SC::WREG - 4);
+  };
+  k_prologue(sa);
+  cur = 0;
   if (ts.n > 1 && ts.n * C::BN <= kLookaheadKeys) {
     // Lookahead.  The first tile is scored for block maxima, and the
     // workgroup votes on whether its rows would crowd their buffers: some
@@ -1161,16 +1203,43 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
     wait_vmcnt<0>();
     if (go) {
       mrun = pair_max(mlook);
-      const double fl = fmax((double)mrun - 1.0, top_floor());
+      float crowd;
+      const double fl = fmax((double)mrun - 1.0, top_floor(&crowd));
       if (!ovf && fl > floor_) set_floor(fl);
+      // A row whose listed block maxima crowd (they take less than kCrowd of
+      // the unit mass above the smallest of them) has a support far larger
+      // than its buffers.  Where most rows of the workgroup do, the
+      // workgroup skips the candidate pass: every row goes to the histogram
+      // and collecting passes at once (its output would run on the matrix
+      // cores anyway); a few such rows alone keep the candidate pass, since
+      // they would cost the whole workgroup its gathered output.  Each wave
+      // posts its counts (crowded rows, rows; both lanes count) in the last
+      // word of its candidate region, which the keyed layout leaves unused,
+      // and the barrier that starts the candidate pass publishes them.
+      if (Lk <= 65535) {
+        const bool crowded = !ovf && crowd < kCrowd;
+        const int nc = __popcll(__ballot(crowded)), nv = __popcll(__ballot(!ovf));
+        if (lane == 0) *vote_word(wave) = (nc << 16) | nv;
+        wait_lgkm0();  // the write lands before the barrier
+        voted = true;
+      }
     }
 #pragma unroll
     for (int i = 0; i < kTop; ++i) top[i] = -INFINITY;
     // every wave is past the last barrier: no stage is being read
     k_prologue(sa);
     cur = 0;
+    if (voted) {
+      int votes = 0;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) votes += *vote_word(w);
+      if (__builtin_expect(2 * (votes >> 16) > (votes & 0xffff), 0)) {
+        ovf = true;
+        run_a = false;
+      }
+    }
   }
-  for (int u = 0; u < ts.n; ++u) {
+  for (int u = 0; run_a && u < ts.n; ++u) {
     const bf16_t* kl = ka_of(cur);
     k_next(sa, u, cur);
     const int t = ts.tile(u);
@@ -1313,27 +1382,13 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   }
 
   // ---- extra passes for rows whose candidates outgrew the buffer -----------
-  // Each pass re-streams the K tiles and, for every pending row, both
-  // accumulates (count, sums, minimum) above the floor and collects the
-  // values above it into the lane buffers.  When both halves fit, the row is
-  // solved exactly from the buffers as above; otherwise the totals give one
-  // threshold step and the next pass starts from the raised floor.
-  // workgroup OR through one word of K stage 0 (idle here: every transfer has
-  // landed, and the closing barrier keeps the next transfers from landing
-  // before every wave has read it); the runtime's __syncthreads_or would
-  // take static LDS on top of the dynamic allocation and cost the second
-  // workgroup per CU
-  int* const any_word = (int*)ka_of(0);
-  auto block_any = [&](bool v) __attribute__((always_inline)) {
-    __syncthreads();
-    if (tid == 0) *(volatile int*)any_word = 0;
-    __syncthreads();
-    if (v) *(volatile int*)any_word = 1;
-    __syncthreads();
-    const bool r = *(volatile int*)any_word != 0;
-    __syncthreads();
-    return r;
-  };
+  // The first (the histogram pass below) brackets each pending row's tau to
+  // a few bins.  Each later pass re-streams the K tiles and, for every
+  // pending row, both accumulates (count, sums, minimum) above the floor and
+  // collects the values above it into the lane buffers.  When both halves
+  // fit, the row is solved exactly from the buffers as above; otherwise the
+  // totals give one threshold step and the next pass starts from the raised
+  // floor.
   // Bracket of a pending row: floor_ <= tau <= ub.  Each pass also takes the
   // totals above hi (floor_ < hi <= ub, +inf at first) and collects only the
   // values in the window (floor_, hi].  When f(hi) <= 0 and the window fits,
@@ -1342,17 +1397,118 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   // f(hi) > 0), the secant through the best known points on both sides
   // bounds tau from above (f is convex), and the next window is the whole
   // bracket when a linear count model says it fits, else its lower part.
-  double hi_ = INFINITY;     // window top (z units)
-  float hi_v = INFINITY;     // the same test in the stored domain
   double ub = (double)mrun;  // point with f(ub) = fub <= 0 known
   double fub = -1.0;         // (no key lies above the row max)
+  double hi_ = INFINITY;     // window top of a pending row (z units)
+  float hi_v = INFINITY;     // the same test in the stored domain
   auto set_hi = [&](double x) __attribute__((always_inline)) {
     hi_ = x;
     const float xf = float_floor(x);
     hi_v = CAP ? xf : raw_floor(xf, cz);
   };
+  // Histogram pass: one K pass that brackets tau to a few bins before the
+  // passes that collect.  A pending row counts its values above the floor
+  // in NBIN bins of width w over (floor, E(NBIN)], E(b) = floor + b w and
+  // E(NBIN) >= row max, as 16-bit counts n_b in LDS (both lanes of a row
+  // add into the same words).  A value counted in bin b lies in
+  // [E(b) - m, E(b + 1) + m], m = w / 1024 far above the rounding of the
+  // bin index, so with g the normalizer's map (x+ or x+^2)
+  //   f(E(b) - m) >= sum over b' > b  of n_b' g((b' - b) w) - 1,
+  //   f(E(b) + m) <= sum over b' >= b of n_b' g((b' - b + 1) w) - 1,
+  // integer sums (exact in fp64) times w or w^2.  The largest E(b) - m where
+  // the first bound is positive lies below tau, the smallest E(b) + m where
+  // the second is not positive lies at or above it, and the next pass
+  // collects the few bins between the two.
+  // Every wave takes part (barriers inside); `part` marks the rows that are
+  // counted, and such a row's floor and window top move to the bracket.
+  // Runs after a full pass over the keys (the row max is final); counts stay
+  // below 2^16 while a row has fewer than 65536 keys.
+  constexpr int NBIN = SC::NBIN;
+  auto hist_pass = [&](bool part) __attribute__((always_inline)) {
+    unsigned* const hist = (unsigned*)((char*)(lds + SC::NX * KT) + wave * SC::WREG_X);
+    // (called where no candidate region or K stage is live)
+    for (int i = lane; i < NBIN * 16 / 4; i += 64) ((u32x4*)hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    float invw = 0.f;
+    bool use = false;
+    if (part && floor_f > -INFINITY && mrun > floor_f) {
+      float iw = (float)((double)NBIN / ((double)mrun - (double)floor_f));
+      for (int i = 0; i < 4 && (double)floor_f + (double)NBIN / (double)iw < (double)mrun; ++i) iw = next_down(iw);
+      use = iw > 0.f && iw < INFINITY && (double)floor_f + (double)NBIN / (double)iw >= (double)mrun;
+      invw = iw;
+    }
+    unsigned* const hrow = hist + l32;  // word j of this row at hrow[32 j]: bins 2j (low half), 2j + 1
+    k_prologue(sx);
+    cur = 0;
+    for (int u = 0; u < ts.n; ++u) {
+      const bf16_t* kl = ka_of(cur);
+      k_next(sx, u, cur);
+      const int t = ts.tile(u);
+      const int k0 = t * C::BN;
+      const bool active = t >= 0 && wave_rows && k0 < wlast.hi && k0 + C::BN > wfirst.lo && __any(use);
+      if (active) {
+        f32x16 s[C::NKB];
+        qk_tile<C>(kl, qreg, l32, g, s);
+        const bool edge = (k0 + C::BN > wfirst.hi) || (k0 < wlast.lo);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+#pragma clang fp contract(off)
+            float v = CAP ? zval<true>(s[kb][r], cz, sc_over_cap, capz) : s[kb][r];
+            if (edge) {
+              const int key = s_key(k0, kb, r, g);
+              if (key < mine.lo || key >= mine.hi) v = -INFINITY;
+            }
+            if (use && v > floor_v) {  // z > floor_f, so the bin position is >= 0
+              const float z = stored_z<CAP>(v, cz);
+              const int bi = min((int)((z - floor_f) * invw), NBIN - 1);
+              atomicAdd(hrow + 32 * (bi >> 1), 1u << ((bi & 1) << 4));
+            }
+          }
+        }
+      }
+      k_done(sx, cur);
+    }
+    wait_vmcnt<0>();
+    if (use) {
+      // walk down from the top bin; (N, P, Q) = sum over the bins above of
+      // n, n d, n d^2 with d the distance in bins to the current bin
+      const bool ent2 = NORM == ATTN_ENTMAX15;
+      const double w = 1.0 / (double)invw, w2 = w * w;
+      double N = 0.0, P = 0.0, Q = 0.0;
+      int blo = -1, bhi = NBIN;
+      for (int j0 = NBIN / 2 - 4; j0 >= 0 && blo < 0; j0 -= 4) {
+        unsigned wd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[i] = hrow[32 * (j0 + i)];
+#pragma unroll
+        for (int i = 3; i >= 0; --i)
+#pragma unroll
+          for (int hf = 1; hf >= 0; --hf) {
+            if (blo < 0) {
+              const int bb = 2 * (j0 + i) + hf;
+              Q += 2.0 * P + N;
+              P += N;
+              N += (double)((wd[i] >> (16 * hf)) & 0xffffu);
+              const double flo = (ent2 ? Q * w2 : P * w) - 1.0;               // bound at E(bb) - m
+              const double fhi = (ent2 ? (Q + 2.0 * P + N) * w2 : (P + N) * w) - 1.0;  // at E(bb) + m
+              if (fhi <= 0.0) bhi = bb;
+              if (flo > 0.0) blo = bb;
+            }
+          }
+      }
+      const double m = w * (1.0 / 1024.0), base = (double)floor_f;
+      if (blo >= 0 && base + blo * w - m > floor_) set_floor(base + blo * w - m);
+      if (bhi < NBIN) set_hi(base + bhi * w + m);
+    }
+  };
+
+  // (the extra passes are marked unlikely so that register allocation
+  // favours the candidate pass; most workgroups never enter them)
+  if (__builtin_expect(Lk <= 65535 && block_any(pending), 0)) hist_pass(pending);
+
   bool first_x = true;
-  while (block_any(pending)) {
+  while (__builtin_expect(block_any(pending), 0)) {
     if (SC::NX != NA && first_x) {
       // pass A's buffers are dead: a wave with a pending row has dropped its
       // keys, so the output runs on the matrix cores
