@@ -776,11 +776,15 @@ __device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, i
   // weight and V row (this lane's half) of entry i (past the end: weight 0
   // and key 0, a row of this sequence whenever any lane of the wave has
   // entries)
+  // (both LDS reads are unconditional, from an entry inside the buffers, so
+  // that the entries of a group issue their reads back to back)
   auto fetch = [&](int i, float& pj, u32x4 (&wj)[NV]) __attribute__((always_inline)) {
     const bool ok = i < n;
-    const int slot = !ok ? 0 : (i < n0 ? lead + i * 64 : lead + 32 + (i - n0) * 64);
+    const int s0 = lead + i * 64, s1 = lead + 32 + (i - n0) * 64;
+    const int slot = ok ? (i < n0 ? s0 : s1) : 0;
     const float v = buf[slot];
-    const int key = ok ? (int)kbuf[slot] : 0;
+    const int kraw = kbuf[slot];
+    const int key = ok ? kraw : 0;
     float pw;
     {
 #pragma clang fp contract(off)
@@ -794,7 +798,7 @@ __device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, i
       const int64_t page = page_of(pg.row, min(key / pg.bs, pg.max_blocks - 1), pg.nblk);
       off = page * v_sb + (int64_t)(key % pg.bs) * v_sl;
     } else {
-      off = (int64_t)key * v_sl;
+      off = (int64_t)((uint32_t)key * (uint32_t)v_sl);  // < 2^31: the slice fits a 32-bit buffer record
     }
     const u32x4* vr = (const u32x4*)(vcol + off);
 #pragma unroll
@@ -823,13 +827,22 @@ __device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, i
       }
   };
   if constexpr (U % 2 == 0) {
-    for (int e = 0; __any(e < n); e += U) {
-      float p[U];
-      u32x4 w[U][NV];
+    // two groups of U entries in flight: the next group's reads are issued
+    // before the current group is added
+    float pa[U], pb[U];
+    u32x4 wa[U][NV], wb[U][NV];
 #pragma unroll
-      for (int j = 0; j < U; ++j) fetch(e + j, p[j], w[j]);
+    for (int j = 0; j < U; ++j) fetch(j, pa[j], wa[j]);
+    for (int e = 0; __any(e < n); e += 2 * U) {
 #pragma unroll
-      for (int j = 0; j < U; j += 2) add_pair(p[j], p[j + 1], w[j], w[j + 1]);
+      for (int j = 0; j < U; ++j) fetch(e + U + j, pb[j], wb[j]);
+#pragma unroll
+      for (int j = 0; j < U; j += 2) add_pair(pa[j], pa[j + 1], wa[j], wa[j + 1]);
+      if (!__any(e + U < n)) break;
+#pragma unroll
+      for (int j = 0; j < U; ++j) fetch(e + 2 * U + j, pa[j], wa[j]);
+#pragma unroll
+      for (int j = 0; j < U; j += 2) add_pair(pb[j], pb[j + 1], wb[j], wb[j + 1]);
     }
   } else {
     for (int e = 0; __any(e < n); e += U) {
