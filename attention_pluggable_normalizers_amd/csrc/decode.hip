@@ -1177,18 +1177,33 @@ __global__ __launch_bounds__(64) void decode_plan_kernel(FwdArgs a, float* ws, i
   const int lane = threadIdx.x;
   float best = -1.f;
   int best_ks = fixed_ks > 0 ? fixed_ks : kSplit;
-  for (int ks = kMinSplit; fixed_ks == 0 && ks <= kMaxSplit; ks += 32) {
-    int items = 0;
+  if (fixed_ks == 0) {
+    // every candidate size's item count from one read of the lengths (a
+    // read per size puts a global-memory round trip per size on this
+    // kernel's critical path)
+    constexpr int NKS = (kMaxSplit - kMinSplit) / 32 + 1;
+    int items[NKS];
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) items[i] = 0;
     for (int b = lane; b < a.B; b += 64) {
       const SeqView sv = seq_view(a, b);
-      if (sv.n > sv.lo) items += (sv.n + ks - 1) / ks - sv.lo / ks;
+      if (sv.n > sv.lo) {
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+          const int ks = kMinSplit + 32 * i;
+          items[i] += (sv.n + ks - 1) / ks - sv.lo / ks;
+        }
+      }
     }
-    items = wave_sum(items) * groups;
-    const float rounds = (float)items / (float)slots;
-    const float eff = rounds <= 0.f ? 0.f : rounds / ceilf(rounds);
-    if (eff >= best) {
-      best = eff;
-      best_ks = ks;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      const int n = wave_sum(items[i]) * groups;
+      const float rounds = (float)n / (float)slots;
+      const float eff = rounds <= 0.f ? 0.f : rounds / ceilf(rounds);
+      if (eff >= best) {  // ascending sizes: the larger one on ties
+        best = eff;
+        best_ks = kMinSplit + 32 * i;
+      }
     }
   }
   // packed list: first live split of each sequence (exclusive prefix sum)
