@@ -1027,23 +1027,71 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
       *crowd = u[M - 1] > -INFINITY ? r : INFINITY;
     }
     const double mref = (double)u[0];
-    double best = -INFINITY, s1 = 0.0, s2 = 0.0;
+    // closed form over the first m values, and whether it lies below the
+    // m-th (then it is that subset's threshold)
+    auto prefix_t = [&](int m, double s1, double s2, double y, bool& ok) __attribute__((always_inline)) {
+      double t;
+      ok = true;
+      if (NORM == ATTN_SPARSEMAX) {
+        t = (s1 - 1.0) / m;
+      } else {
+        const double mu = s1 / m;
+        const double d = (1.0 - (s2 - s1 * mu)) / m;
+        ok = d >= 0.0;
+        t = ok ? mu - sqrt(d) : 0.0;
+      }
+      ok = ok && t < y;
+      return t;
+    };
+    // The thresholds of the consistent prefixes grow with m, so the subset
+    // threshold is taken at the largest prefix that passes the same test
+    // multiplied through by m (no division or root per prefix): sparsemax
+    // s1 - 1 < m y; 1.5-entmax, with q = m (1 - s2) + s1^2 = m^2 d,
+    // q >= 0 and (s1 - m y)^2 < q (s1 - m y >= 0: y is the prefix's
+    // smallest).  That prefix's closed form is then checked as before; if
+    // rounding makes the two tests disagree, every prefix is tried.
+    double s1 = 0.0, s2 = 0.0, s1s = 0.0, s2s = 0.0, ys = 0.0;
+    int ms = 0;
 #pragma unroll
     for (int m = 1; m <= M; ++m) {
       if (!(u[m - 1] > -INFINITY)) break;
       const double y = (double)u[m - 1] - mref;
       s1 += y;
       s2 += y * y;
-      double t;
+      bool pass;
       if (NORM == ATTN_SPARSEMAX) {
-        t = (s1 - 1.0) / m;
+        pass = s1 - 1.0 < m * y;
       } else {
-        const double mu = s1 / m;
-        const double d = (1.0 - (s2 - s1 * mu)) / m;
-        if (d < 0.0) break;
-        t = mu - sqrt(d);
+        const double q = m * (1.0 - s2) + s1 * s1;
+        if (q < 0.0) break;
+        const double a = s1 - m * y;
+        pass = a * a < q;
       }
-      if (t < y) best = fmax(best, t);
+      if (pass) {
+        ms = m;
+        s1s = s1;
+        s2s = s2;
+        ys = y;
+      }
+    }
+    double best = -INFINITY;
+    bool ok = false;
+    if (ms > 0) {
+      const double t = prefix_t(ms, s1s, s2s, ys, ok);
+      if (ok) best = t;
+    }
+    if (ms > 0 && !ok) {
+      s1 = s2 = 0.0;
+      for (int m = 1; m <= M; ++m) {
+        if (!(u[m - 1] > -INFINITY)) break;
+        const double y = (double)u[m - 1] - mref;
+        s1 += y;
+        s2 += y * y;
+        bool okm;
+        const double t = prefix_t(m, s1, s2, y, okm);
+        if (NORM != ATTN_SPARSEMAX && !(1.0 - (s2 - s1 * (s1 / m)) >= 0.0)) break;
+        if (okm) best = fmax(best, t);
+      }
     }
     return mref + best;
   };
