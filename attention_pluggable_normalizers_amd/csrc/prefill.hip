@@ -818,8 +818,9 @@ __device__ __forceinline__ void gather_rows(const float* buf, const u16* kbuf, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const unsigned a0 = w0[c][q], a1 = w1[c][q];
-        const unsigned lo = (a0 & 0xffffu) | (a1 << 16);      // dim 2q of both
-        const unsigned hi = (a0 >> 16) | (a1 & 0xffff0000u);  // dim 2q + 1 of both
+        // byte permutes (bytes 0-3 of the second operand, 4-7 of the first)
+        const unsigned lo = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // dim 2q of both
+        const unsigned hi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // dim 2q + 1 of both
         acc[8 * c + 2 * q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lo), pb,
                                                              acc[8 * c + 2 * q], false);
         acc[8 * c + 2 * q + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), pb,
