@@ -24,6 +24,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
+# The forward kernels keep matrix-product accumulators in VGPRs: at head dim
+# 256 the compiler's AGPR form would move the O accumulators between the two
+# register files at every key tile and need more than the 256 registers that
+# two waves per SIMD allow.
+PER_FILE = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():
@@ -35,7 +40,7 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -102,7 +102,13 @@ struct DmaTiles {
   static constexpr int ROWS = 64 / C::CPR;        // tile rows one transfer covers
   static_assert(C::KCH % (64 * C::NW) == 0, "K/V tile must split into 1 KB transfers per wave");
   static constexpr int PER_TILE = 2 * NI;         // vmcnt events per tile
-  uint32_t ko[NI], vo[NI];                        // per-lane byte offsets inside a tile
+  // Transfer i of a wave covers tile rows RSTEP i + (its rows of transfer 0).
+  // The swizzles repeat every 16 rows (K) and 4 rows (V), so the lane's
+  // offsets of transfer i are those of transfer i mod 2 (K) or 0 (V) plus
+  // RSTEP i rows, which go to the scalar offset: three VGPRs instead of 2 NI.
+  static constexpr int RSTEP = C::NW * ROWS;
+  static_assert((2 * RSTEP) % 16 == 0 && RSTEP % 4 == 0, "swizzles must repeat across transfers");
+  uint32_t ko0, ko1, vo0;                         // per-lane byte offsets (transfers 0, 1; V: 0)
   uint32_t kstr, vstr;
   int wave;                                       // wave-uniform
 
@@ -110,14 +116,13 @@ struct DmaTiles {
     kstr = (uint32_t)(ksl * 2);
     vstr = (uint32_t)(vsl * 2);
     wave = wave_u;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int pos = (i * C::NW + wave) * 64 + lane;  // LDS chunk this lane fills
-      const int row = pos / C::CPR, pc = pos % C::CPR;
-      ko[i] = row * kstr + k_chunk<C::D>(row, pc) * 16;
-      vo[i] = row * vstr + (pc ^ v_swz<C>(row)) * 16;
-    }
+    const int pos = wave * 64 + lane;  // LDS chunk this lane fills in transfer 0
+    const int row = pos / C::CPR, pc = pos % C::CPR;
+    ko0 = row * kstr + k_chunk<C::D>(row, pc) * 16;
+    ko1 = row * kstr + k_chunk<C::D>(row + RSTEP, pc) * 16;
+    vo0 = row * vstr + (pc ^ v_swz<C>(row)) * 16;
   }
+  __device__ __forceinline__ uint32_t ko(int i) const { return (i & 1) ? ko1 : ko0; }
   // paged: byte offset of transfer i's first key and the records up to the
   // sequence's last key (0 when none of its keys is live)
   __device__ __forceinline__ void page_span(const PageCtx& pg, int key0, bool live, uint32_t kstride,
@@ -144,14 +149,14 @@ struct DmaTiles {
     if (!pg.row) {
       const uint32_t ks = live ? (uint32_t)k0 * kstr : 0x80000000u;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
+      for (int i = 0; i < NI; ++i) dma16(rk, kla + i * C::NW * 1024, ko(i), ks + (uint32_t)(i * RSTEP) * kstr);
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int r0 = (i * C::NW + wave) * ROWS;
         uint32_t ks, kn;
         page_span(pg, k0 + r0, live, kstr, pg.kpage, ks, kn);
-        dma16(with_records(rk, kn), kla + i * C::NW * 1024, ko[i] - (uint32_t)r0 * kstr, ks);
+        dma16(with_records(rk, kn), kla + i * C::NW * 1024, ko(i) - (uint32_t)(r0 - i * RSTEP) * kstr, ks);
       }
     }
   }
@@ -163,8 +168,8 @@ struct DmaTiles {
       const uint32_t vs = live ? (uint32_t)k0 * vstr : 0x80000000u;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        dma16(rk, kla + i * C::NW * 1024, ko[i], ks);
-        dma16(rv, vla + i * C::NW * 1024, vo[i], vs);
+        dma16(rk, kla + i * C::NW * 1024, ko(i), ks + (uint32_t)(i * RSTEP) * kstr);
+        dma16(rv, vla + i * C::NW * 1024, vo0, vs + (uint32_t)(i * RSTEP) * vstr);
       }
     } else {
 #pragma unroll
@@ -173,8 +178,8 @@ struct DmaTiles {
         uint32_t ks, kn, vs, vn;
         page_span(pg, k0 + r0, live, kstr, pg.kpage, ks, kn);
         page_span(pg, k0 + r0, live, vstr, pg.vpage, vs, vn);
-        dma16(with_records(rk, kn), kla + i * C::NW * 1024, ko[i] - (uint32_t)r0 * kstr, ks);
-        dma16(with_records(rv, vn), vla + i * C::NW * 1024, vo[i] - (uint32_t)r0 * vstr, vs);
+        dma16(with_records(rk, kn), kla + i * C::NW * 1024, ko(i) - (uint32_t)(r0 - i * RSTEP) * kstr, ks);
+        dma16(with_records(rv, vn), vla + i * C::NW * 1024, vo0 - (uint32_t)(r0 - i * RSTEP) * vstr, vs);
       }
     }
   }
@@ -240,18 +245,22 @@ __device__ __forceinline__ PageCtx page_ctx(const FwdArgs& a, int b, int Lk) {
 // keys its half of the P operand holds (S^T accumulator layout).
 template <class C>
 struct VTr {
-  uint32_t off[C::NDB];  // byte offset of this lane's first read for step 0
+  // The V swizzle only permutes 16-byte chunks within groups of four, so dim
+  // block db reads at the offset of block db mod 4 plus (db / 4) * 256 bytes
+  // (a constant of the LDS instruction): at most four VGPRs per lane.
+  static constexpr int NO = C::NDB < 4 ? C::NDB : 4;
+  uint32_t off[NO];  // byte offset of this lane's first read for step 0, dim blocks 0 .. NO - 1
   __device__ __forceinline__ void init(int lane) {
     const int G = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
     const int r0 = 4 * (G >> 1) + j;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
+    for (int db = 0; db < NO; ++db) {
       const int lc = db * 4 + 2 * (G & 1) + (q >> 1);
       off[db] = (uint32_t)((r0 * C::D + (lc ^ v_swz<C>(r0)) * 8 + (q & 1) * 4) * 2);
     }
   }
   __device__ __forceinline__ bf16x8 read(const bf16_t* vl, int t, int db) const {
-    const char* p = (const char*)vl + off[db] + t * 16 * C::D * 2;
+    const char* p = (const char*)vl + off[db & 3] + (db >> 2) * 256 + t * 16 * C::D * 2;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)(p + 8 * C::D * 2));
@@ -261,7 +270,7 @@ struct VTr {
 
 // GEN: paged K/V or a block mask (tile sequence and page lookups compiled in)
 template <class C, int NBUF, int NORM, bool CAP, bool GEN>
-__global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_softmax_kernel(FwdArgs a) {
+__global__ __launch_bounds__(C::NT, 2) void prefill_softmax_kernel(FwdArgs a) {
   static_assert(NBUF == 2 || NBUF == 3, "two or three tiles in flight");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NBUF * 2 * C::BN * C::D];
 
