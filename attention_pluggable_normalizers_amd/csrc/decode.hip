@@ -497,8 +497,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(FwdArgs a, float* ws, 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
+// POLICY: the load's cache policy bits (2: non-temporal, for data read once)
+template <int POLICY = 0>
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POLICY));
 }
 
 // Split kernel for caches whose page size is a multiple of 16 keys, so a
@@ -518,6 +520,9 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
   constexpr int KS = 64 / CPR;    // key rows per PV step (lanes per chunk column)
   constexpr int RPB = 16 / KS;    // V rows per lane per 16-key block
   constexpr int NV = 32 / KS;     // V rows per lane per 32-key chunk
+  // The softmax family reads every K/V byte once: non-temporal loads (the
+  // sparse split kernel measured faster with the default policy).
+  constexpr int kPolicy = SPARSE ? 0 : 2;
 
   // A workgroup is WPG waves on WPG consecutive kv heads of one split, so the
   // slot rows of a page (all heads side by side) are read together; the
@@ -598,7 +603,7 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
       const __amdgpu_buffer_rsrc_t rk = block_rsrc(kaddr, kbytes, 2 * t + sb);
 #pragma unroll
       for (int c = 0; c < NKC; ++c)
-        kt[sb][c] = __builtin_bit_cast(bf16x8, buf_load16(rk, k_voff + 64 * c, 0));
+        kt[sb][c] = __builtin_bit_cast(bf16x8, buf_load16<kPolicy>(rk, k_voff + 64 * c, 0));
     }
   };
   // scores of chunk t in z units (sparse) or log2 units (softmax family);
@@ -672,7 +677,7 @@ __global__ __launch_bounds__(512) void decode_split_paged16_kernel(FwdArgs a, fl
     for (int sb = 0; sb < 2; ++sb) {
       const __amdgpu_buffer_rsrc_t rv = block_rsrc(vaddr, vbytes, 2 * t + sb);
 #pragma unroll
-      for (int i = 0; i < RPB; ++i) vr[sb * RPB + i] = buf_load16(rv, v_voff, i * v_step);
+      for (int i = 0; i < RPB; ++i) vr[sb * RPB + i] = buf_load16<kPolicy>(rv, v_voff, i * v_step);
     }
   };
   float acc[GM][8];
