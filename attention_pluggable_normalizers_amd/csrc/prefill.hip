@@ -270,7 +270,7 @@ struct VTr {
 
 // GEN: paged K/V or a block mask (tile sequence and page lookups compiled in)
 template <class C, int NBUF, int NORM, bool CAP, bool GEN>
-__global__ __launch_bounds__(C::NT, 2) void prefill_softmax_kernel(FwdArgs a) {
+__global__ __launch_bounds__(C::NT, C::D == 64 ? 4 : 2) void prefill_softmax_kernel(FwdArgs a) {
   static_assert(NBUF == 2 || NBUF == 3, "two or three tiles in flight");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NBUF * 2 * C::BN * C::D];
 
@@ -342,15 +342,9 @@ __global__ __launch_bounds__(C::NT, 2) void prefill_softmax_kernel(FwdArgs a) {
   // weights of one tile from its raw scores s, then O += V^T P^T
   auto consume = [&](f32x16 (&s)[C::NKB], int t, const bf16_t* vl) __attribute__((always_inline)) {
     const int k0 = t * C::BN;
-    constexpr int NV = C::NDB * 2 * C::NKB;
-    constexpr bool kPreV = NV <= 8;  // V operands fit in registers across the softmax
-    bf16x8 vop[kPreV ? NV : 1];
-    if constexpr (kPreV) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int u = 0; u < 2 * C::NKB; ++u) vop[db * 2 * C::NKB + u] = vtr.read(vl, u, db);
-    }
+    // (the V operands are read right before their products: held across the
+    // softmax they would take the registers of a fourth wave per SIMD at
+    // head dim 64)
     if (CAP) {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
@@ -410,7 +404,7 @@ __global__ __launch_bounds__(C::NT, 2) void prefill_softmax_kernel(FwdArgs a) {
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int u = 0; u < 2 * C::NKB; ++u)
-        o[db] = mfma(kPreV ? vop[db * 2 * C::NKB + u] : vtr.read(vl, u, db), pk[u], o[db]);
+        o[db] = mfma(vtr.read(vl, u, db), pk[u], o[db]);
   };
 
   const i32x4 rk = rsrc_words(kbase, (uint32_t)((int64_t)Lk * a.k_sl * 2));
@@ -1853,9 +1847,10 @@ __global__ __launch_bounds__(C::NT, (C::D <= 128 ? 2 : 1)) void prefill_sparse_k
   }
 }
 
-// K/V tiles in flight per workgroup (LDS: NBUF * 2 * BN * D * 2 bytes)
+// K/V tiles in flight per workgroup (LDS: NBUF * 2 * BN * D * 2 bytes; two
+// keep four workgroups per CU at head dim 64, two at 128 and 256)
 template <class C>
-constexpr int kStages = C::D == 64 ? 3 : 2;
+constexpr int kStages = 2;
 
 template <class C, int NORM>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
