@@ -27,8 +27,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 # The forward kernels keep matrix-product accumulators in VGPRs: at head dim
 # 256 the compiler's AGPR form would move the O accumulators between the two
 # register files at every key tile and need more than the 256 registers that
-# two waves per SIMD allow.
-PER_FILE = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# two waves per SIMD allow.  On finite inputs their device code never makes a
+# NaN (the API rejects non-finite scaling and softcap; masked scores are -inf,
+# and cache slots past a sequence read as zeros), so it is compiled without
+# NaN semantics: a max then needs no canonicalizing instruction per operand
+# that is not known to be canonical.  (Inputs holding NaN give undefined
+# outputs either way.)  Host code keeps full IEEE semantics.
+PER_FILE = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Xarch_device", "-fno-honor-nans"]}
 
 
 def _hipcc():

@@ -38,11 +38,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# sources of the prefill kernels (the counter summary is tied to their hash)
+# sources of the prefill kernels and the build script that sets their
+# compiler flags (the counter summary is tied to their hash)
+_BUILD_PY = os.path.join(ROOT, "attention_pluggable_normalizers_amd", "build.py")
 PREFILL_SRCS = [os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", f)
-                for f in ("prefill.hip", "tiles.h", "common.h")]
+                for f in ("prefill.hip", "tiles.h", "common.h")] + [_BUILD_PY]
 DECODE_SRCS = [os.path.join(ROOT, "attention_pluggable_normalizers_amd", "csrc", f)
-               for f in ("decode.hip", "common.h")]
+               for f in ("decode.hip", "common.h")] + [_BUILD_PY]
 
 
 def credited_pairs(cfg):
